@@ -1,0 +1,186 @@
+"""Benchmark: one decode step of the paged MLA hot path on one MI355X.
+
+A step is the whole path on one batch: mla_get_metadata, mla_absorb_q,
+mla_decode_paged (split kernel + combine) and mla_up_v. Inputs are seeded
+synthetic tensors already resident in HBM. To keep the 256 MB Infinity Cache
+from serving repeats, R copies of every input and output rotate, with R times
+the working set above 1 GiB.
+
+Prints one JSON line (rank 0, N = 1). Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config full_heads]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode µs/call + latent-KV TB/s + TFLOPS (% roofline), b=128 h=128"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def algorithmic_work(inp):
+    """Bytes and flops the decode call must move and compute (no re-reads, no partials)."""
+    import numpy as np
+    L = np.maximum(inp.seqlens.astype(np.int64), 0)
+    rows = inp.b * inp.s_q * inp.h
+    pages = (L + 63) // 64
+    kv_bytes = int(L.sum()) * 1152
+    q_bytes = rows * (512 + 64) * 2
+    out_bytes = rows * (512 * 2 + 4)
+    int_bytes = 4 * int(pages.sum()) + 4 * inp.b
+    keys = 0
+    for j in range(inp.s_q):
+        n = L - inp.s_q + 1 + j if inp.causal else L
+        keys += int(np.maximum(n, 0).sum())
+    flops = 2 * inp.h * keys * (576 + 512)
+    return dict(kv_bytes=kv_bytes, bytes=kv_bytes + q_bytes + out_bytes + int_bytes, flops=flops)
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the CPU oracle as it stands on a bounded sample and scale to one call."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import mla_oracle as O
+    order = np.argsort(inp.seqlens)
+    seqs = [int(order[len(order) // 2])]  # a median-length sequence
+    heads = list(range(inp.h))
+    done_heads = 0
+    t0 = time.perf_counter()
+    for hd in heads:  # one head at a time until the budget is spent
+        O.decode_naive_inputs(inp, seqs=seqs, heads=[hd])
+        done_heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    L = np.maximum(inp.seqlens.astype(np.int64), 0)
+    frac = float(L[seqs].sum()) * done_heads / (float(L.sum()) * inp.h)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": dt / frac * 1e6, "unit": "us/call", "cores": int(threads), "kind": "oracle",
+            "sample": f"naive fp64 oracle on sequence {seqs[0]} (L={int(L[seqs[0]])}), {done_heads} of {inp.h} "
+                      f"heads, {dt:.1f} s, scaled by key-head count to the full call"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="full_heads")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path does not shard "
+              "across GPUs in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_decode_paged_amd as mla
+    from mla_inputs import CONFIGS, make_inputs
+
+    torch.cuda.set_device(0)
+    mla.load()
+    inp = make_inputs(args.config, seed=args.seed)
+    work = algorithmic_work(inp)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def dev_i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    kv0 = dev_bf16(inp.kv_cache)
+    working = kv0.numel() * 2 + inp.b * inp.s_q * inp.h * (576 + 512 + 512) * 2
+    R = max(1, math.ceil((1 << 30) / working))
+    sets = []
+    for r in range(R):
+        sets.append(dict(
+            kv=kv0 if r == 0 else kv0.clone(), bt=dev_i32(inp.block_table), sl=dev_i32(inp.seqlens),
+            q_nope=dev_bf16(inp.q_nope), q_pe=dev_bf16(inp.q_pe), w_uk=dev_bf16(inp.w_uk),
+            w_uv=dev_bf16(inp.w_uv),
+            q_lat=torch.empty((inp.b, inp.s_q, inp.h, 512), dtype=torch.bfloat16, device="cuda"),
+            q_lo=torch.empty((inp.b, inp.s_q, inp.h, 512), dtype=torch.bfloat16, device="cuda"),
+            o_lat=torch.empty((inp.b, inp.s_q, inp.h, 512), dtype=torch.bfloat16, device="cuda"),
+            lse=torch.empty((inp.b, inp.s_q, inp.h), dtype=torch.float32, device="cuda"),
+            o=torch.empty((inp.b, inp.s_q, inp.h, 128), dtype=torch.bfloat16, device="cuda")))
+    slots = mla.num_slots(inp.b, inp.s_q, inp.h)
+    ws = torch.empty((mla.workspace_bytes(inp.b, inp.s_q, inp.h, slots),), dtype=torch.uint8, device="cuda")
+    metas = [mla.get_metadata(s["sl"], slots, s_q=inp.s_q, h=inp.h) for s in sets]
+
+    ev = {k: [] for k in ("meta", "absorb", "decode", "up_v")}
+
+    def step(i, timed):
+        s = sets[i % R]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
+        if timed:
+            e[0].record()
+        meta, ns = mla.get_metadata(s["sl"], slots, s_q=inp.s_q, h=inp.h)
+        if timed:
+            e[1].record()
+        mla.absorb_q(s["q_nope"], s["w_uk"], out=(s["q_lat"], s["q_lo"]))
+        if timed:
+            e[2].record()
+        mla.decode_paged(s["q_lat"], s["q_pe"], s["kv"], s["bt"], s["sl"], meta, ns, inp.scale, inp.causal,
+                         q_lat_lo=s["q_lo"], workspace=ws, out=(s["o_lat"], s["lse"]))
+        if timed:
+            e[3].record()
+        mla.up_v(s["o_lat"], s["w_uv"], out=s["o"])
+        if timed:
+            e[4].record()
+            for k, a, b in (("meta", 0, 1), ("absorb", 1, 2), ("decode", 2, 3), ("up_v", 3, 4)):
+                ev[k].append((e[a], e[b]))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert mla.take_device_error() == 0
+    us = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in ev.items()}
+    us_step = wall / args.steps * 1e6
+
+    t_dec = us["decode"] * 1e-6
+    achieved = work["bytes"] / t_dec / 1e9
+    tflops = work["flops"] / t_dec / 1e12
+    cfg = CONFIGS[args.config]
+    line = {
+        "metric": METRIC, "value": round(us_step, 3), "unit": "us/call", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config}: b={inp.b} h={inp.h} s_q={inp.s_q} causal={inp.causal} "
+                               f"seqlens={cfg['seqlens']} sum_L={int(inp.seqlens.sum())} page=64 row=576 bf16 "
+                               f"seed={args.seed}",
+                   "num_slots": slots, "rotating_copies": R},
+        "stage_us": {k: round(v, 3) for k, v in us.items()},
+        "decode_us": round(us["decode"], 3),
+        "latent_kv_TBps": round(work["kv_bytes"] / t_dec / 1e12, 4),
+        "decode_TFLOPs": round(tflops, 2),
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_decode_paged call (split kernel + combine)",
+                     "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"]},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+"""Python binding of libmla (include/mla.h): paged MLA decode on MI355X.
+
+Argument marshalling only. Every step runs in the HIP kernels of libmla.so;
+PyTorch supplies device memory and the current stream. Nothing here computes
+on the CPU, and every call raises if the library is missing or returns an
+error.
+
+One decode step of one layer:
+
+    tile_meta, num_splits = get_metadata(cache_seqlens)          # once per step
+    q_lat, q_lat_lo = absorb_q(q_nope, w_uk)
+    o_lat, lse = decode_paged(q_lat, q_pe, kv_cache, block_table, cache_seqlens,
+                              tile_meta, num_splits, softmax_scale, causal,
+                              q_lat_lo=q_lat_lo)
+    o = up_v(o_lat, w_uv)
+
+bf16 tensors are torch.bfloat16 (int16/uint16 views are accepted too).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "decode_paged",
+           "up_v", "gather_pages", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
+           "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE", "LO_PASS_MAX_LEN"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+PAGE_TOKENS, D_LATENT, D_ROPE, D_ROW, D_NOPE = 64, 512, 64, 576, 128
+LO_PASS_MAX_LEN = 1024
+META_WORDS = 8
+# fixed cost of one sequence piece in the split plan, in pages
+SPLIT_OVERHEAD = 2
+
+_lib = None
+_P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class MLAError(RuntimeError):
+    pass
+
+
+def load():
+    """Load libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MLAError(f"{LIB_PATH} is missing: build it with `python -m mla_decode_paged_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "mla_last_error": (ctypes.c_char_p, []),
+        "mla_num_slots": (_I, [_I, _I, _I, ctypes.POINTER(_I)]),
+        "mla_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+        "mla_get_metadata": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+        "mla_absorb_q": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
+        "mla_decode_paged": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
+                                  _P, _P, _P]),
+        "mla_up_v": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+        "mla_gather_pages": (_I, [_P, _I64, _P, _I, _P, _I, _P, _P, _P]),
+        "mla_take_device_error": (_I, [ctypes.POINTER(_I)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().mla_last_error().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise MLAError(f"{what} failed ({rc}): {last_error()}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtypes=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MLAError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MLAError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise MLAError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MLAError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+
+
+def num_slots(b: int, s_q: int, h: int) -> int:
+    out = _I(0)
+    _check(load().mla_num_slots(b, s_q, h, ctypes.byref(out)), "mla_num_slots")
+    return out.value
+
+
+def workspace_bytes(b: int, s_q: int, h: int, slots: int) -> int:
+    n = load().mla_workspace_bytes(b, s_q, h, slots)
+    if n == 0:
+        raise MLAError("mla_workspace_bytes: bad arguments")
+    return n
+
+
+def get_metadata(cache_seqlens: torch.Tensor, slots: int | None = None, s_q: int = 1, h: int = 128,
+                 split_overhead: int = SPLIT_OVERHEAD):
+    """Split-KV plan: (tile_meta int32 [slots, 8], num_splits int32 [b + 1])."""
+    b = cache_seqlens.numel()
+    if slots is None:
+        slots = num_slots(b, s_q, h)
+    dev = cache_seqlens.device
+    tile_meta = torch.empty((slots, META_WORDS), dtype=torch.int32, device=dev)
+    num_splits = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    _check(load().mla_get_metadata(_ptr(cache_seqlens, "cache_seqlens", _I32), b, slots, split_overhead,
+                                   _ptr(tile_meta, "tile_meta"), _ptr(num_splits, "num_splits"), _stream()),
+           "mla_get_metadata")
+    return tile_meta, num_splits
+
+
+def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, lo: bool = True, out=None):
+    """q_lat = q_nope @ W_UK per head, bf16 (and its bf16 rounding residue if lo)."""
+    b, s_q, h, dn = q_nope.shape
+    dev = q_nope.device
+    if out is None:
+        q_lat = torch.empty((b, s_q, h, D_LATENT), dtype=torch.bfloat16, device=dev)
+        q_lo = torch.empty_like(q_lat) if lo else None
+    else:
+        q_lat, q_lo = out
+    _check(load().mla_absorb_q(_ptr(q_nope, "q_nope", _BF16, (b, s_q, h, D_NOPE)),
+                               _ptr(w_uk, "w_uk", _BF16, (h, D_NOPE, D_LATENT)),
+                               _ptr(q_lat, "q_lat", _BF16, (b, s_q, h, D_LATENT)),
+                               _ptr(q_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)), b, s_q, h, _stream()),
+           "mla_absorb_q")
+    return q_lat, q_lo
+
+
+def decode_paged(q_lat, q_pe, kv_cache, block_table, cache_seqlens, tile_meta, num_splits, softmax_scale,
+                 causal, q_lat_lo=None, workspace=None, out=None):
+    """Paged absorbed-form decode: (o_lat bf16 [b, s_q, h, 512], lse fp32 [b, s_q, h])."""
+    b, s_q, h, _ = q_lat.shape
+    slots = tile_meta.shape[0]
+    dev = q_lat.device
+    need = workspace_bytes(b, s_q, h, slots)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if out is None:
+        o_lat = torch.empty((b, s_q, h, D_LATENT), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((b, s_q, h), dtype=torch.float32, device=dev)
+    else:
+        o_lat, lse = out
+    if kv_cache.dim() != 3 or tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_ROW):
+        raise MLAError(f"kv_cache must be [num_pages, {PAGE_TOKENS}, {D_ROW}]")
+    _check(load().mla_decode_paged(
+        _ptr(q_lat, "q_lat", _BF16), _ptr(q_lat_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)),
+        _ptr(q_pe, "q_pe", _BF16, (b, s_q, h, D_ROPE)), _ptr(kv_cache, "kv_cache", _BF16), kv_cache.shape[0],
+        _ptr(block_table, "block_table", _I32), block_table.shape[1],
+        _ptr(cache_seqlens, "cache_seqlens", _I32, (b,)), b, s_q, h, float(softmax_scale), int(bool(causal)),
+        _ptr(tile_meta, "tile_meta", _I32), _ptr(num_splits, "num_splits", _I32, (b + 1,)), slots,
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(o_lat, "o_lat", _BF16, (b, s_q, h, D_LATENT)), _ptr(lse, "lse", (torch.float32,), (b, s_q, h)),
+        _stream()), "mla_decode_paged")
+    return o_lat, lse
+
+
+def up_v(o_lat: torch.Tensor, w_uv: torch.Tensor, out=None):
+    """o = o_lat @ W_UV per head, bf16 [b, s_q, h, 128]."""
+    b, s_q, h, _ = o_lat.shape
+    o = out if out is not None else torch.empty((b, s_q, h, D_NOPE), dtype=torch.bfloat16, device=o_lat.device)
+    _check(load().mla_up_v(_ptr(o_lat, "o_lat", _BF16, (b, s_q, h, D_LATENT)),
+                           _ptr(w_uv, "w_uv", _BF16, (h, D_LATENT, D_NOPE)),
+                           _ptr(o, "o", _BF16, (b, s_q, h, D_NOPE)), b, s_q, h, _stream()), "mla_up_v")
+    return o
+
+
+def gather_pages(kv_cache, block_table, cache_seqlens, row_offsets, total_rows: int):
+    """Rows of every cached token, in order, through the decode kernel's page loader."""
+    b = cache_seqlens.numel()
+    out = torch.empty((max(total_rows, 1), D_ROW), dtype=torch.bfloat16, device=kv_cache.device)
+    _check(load().mla_gather_pages(_ptr(kv_cache, "kv_cache", _BF16), kv_cache.shape[0],
+                                   _ptr(block_table, "block_table", _I32), block_table.shape[1],
+                                   _ptr(cache_seqlens, "cache_seqlens", _I32), b,
+                                   _ptr(row_offsets, "row_offsets", (torch.int64,), (b,)), _ptr(out, "out"),
+                                   _stream()), "mla_gather_pages")
+    return out[:total_rows]
+
+
+def take_device_error() -> int:
+    """MLA_DEVERR_* bits raised by kernels since the last call (synchronises)."""
+    bits = _I(0)
+    _check(load().mla_take_device_error(ctypes.byref(bits)), "mla_take_device_error")
+    return bits.value

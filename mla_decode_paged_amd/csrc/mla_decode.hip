@@ -1,0 +1,562 @@
+// Paged MLA decode in the absorbed form (gfx950).
+//
+// What is computed: for every query row r = (j, i) of sequence b, scores
+// s_t = scale * (q_lat[r] . c_t + q_pe[r] . kpe_t) against each visible cached
+// token t (the latent c_t and rotated positional key kpe_t share one 576-wide
+// row: "DeepSeek-V3 Multi-head Latent Attention (MLA) 深度工程", sections 2.4
+// and 3.1), an exact softmax kept in streaming form (the same page's section
+// 4.1 recurrence), o_lat[r] = sum_t p_t c_t and lse[r].
+//
+// How it maps onto MI355X (one workgroup = NW wavefronts, 32 query rows each):
+//  * Page loader. A page is 64 rows x 1152 contiguous bytes. It is copied
+//    straight from HBM into LDS with 16-byte direct-to-LDS loads
+//    (global_load_lds_dwordx4): 73 wave instructions of 1 KB each cover the
+//    64 rows at a padded LDS row stride of 1168 bytes (the 73rd 16-byte slot of
+//    each LDS row is padding). Two page buffers alternate, so the next page
+//    streams in while the current one is multiplied; this is the double
+//    buffer of the SC11 note's Page Attention figure, done by the CU's own
+//    load path instead of separate DMA engines. Tokens past the cache length
+//    and bad page ids load a zero row, so NaN or stale data never reach LDS.
+//  * QK^T on the matrix cores, transposed: S^T[token, row] = K Q^T with K
+//    (the page rows) as the A operand read from LDS and Q as the B operand
+//    held in VGPRs for the whole piece. Each lane then owns 16 scores of ONE
+//    query row per 32-token tile, so the row max and row sum are in-lane plus
+//    a single exchange between lanes l and l + 32.
+//  * The probabilities come out of the score accumulators already in the
+//    B-operand layout of the next product, so PV needs no shuffle:
+//    O^T[d, row] += V^T P^T, with V^T read from the same LDS page by
+//    transposed reads (ds_read_b64_tr_b16). V is columns 0..511 of the row.
+//  * Online softmax in base 2 with the scale folded in, against a fixed
+//    per-row reference (the row's first tile max) instead of the running
+//    max: any reference gives the exact result, fp32 has the range for
+//    exp2(x - m_ref) up to 2^64, and the 256 accumulators then never need a
+//    rescale (so they stay pinned in AGPRs). A score more than 2^64 above the
+//    reference makes the workgroup recompute the piece with a larger one.
+//  * Split-KV: the planner hands each workgroup slot a contiguous run of
+//    pages (possibly spanning several sequences). A sequence held by one slot
+//    is finalised in place; otherwise each piece writes an fp32 partial (O/l,
+//    lse) and mla_combine merges them by lse rescaling.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "mla_device.h"
+#include "mla_host.h"
+
+namespace mla {
+
+__device__ int g_device_error = 0;
+__device__ const uint4 g_zero_row[kRowBytes / 16] = {};
+
+constexpr int kLdsRowStride = kRowBytes + 16;              // 1168
+constexpr int kLdsSlotsPerRow = kLdsRowStride / 16;         // 73
+constexpr int kStageBytes = kPage * kLdsRowStride;          // 74752
+constexpr int kLoadInstrPerPage = kPage * kLdsSlotsPerRow / 64;  // 73
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource: dword data, bounds-checked
+constexpr float kRefSlack = 64.0f;  // log2 units a score may exceed the softmax reference
+
+static_assert(kPage * kLdsSlotsPerRow % 64 == 0, "page must fill whole wave loads");
+
+struct DecodeParams {
+  const uint16_t* q_lat;
+  const uint16_t* q_lat_lo;
+  const uint16_t* q_pe;
+  const uint16_t* kv;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* tile_meta;
+  const int32_t* num_splits;
+  float* part_o;
+  float* part_lse;
+  uint16_t* o_lat;
+  float* lse;
+  long long num_pages;
+  int max_blocks, b, s_q, h, log2_h, M, n_rowblocks, num_slots, causal;
+  float scale_log2e;
+};
+
+__device__ __forceinline__ void flag_error(int bit) { atomicOr(&g_device_error, bit); }
+
+// Issue this wave's share of the direct-to-LDS loads of one page.
+// nvalid: rows of the page that hold tokens (< 64 on the last page).
+// Every lane runs the same instructions: the source address is chosen by a
+// bit select, never by a branch (see the note on divergence at the kernel).
+template <int NW>
+__device__ __forceinline__ void issue_page(const char* page_base, bool page_ok, int nvalid,
+                                           MLA_LDS char* stage, int wave, int lane) {
+  const uintptr_t zero = reinterpret_cast<uintptr_t>(g_zero_row);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(page_base);
+#pragma unroll 1
+  for (int inst = wave; inst < kLoadInstrPerPage; inst += NW) {
+    const int s = inst * 64 + lane;
+    const int row = s / kLdsSlotsPerRow;
+    const int c = s - row * kLdsSlotsPerRow;
+    const bool real = page_ok && row < nvalid && c < kLdsSlotsPerRow - 1;
+    const uintptr_t a = base + (uintptr_t)(row * kRowBytes + c * 16);
+    const uintptr_t z = zero + (uintptr_t)((c & 63) * 16);
+    const uintptr_t m = (uintptr_t)0 - (uintptr_t)real;
+    g2lds16(reinterpret_cast<const void*>(z ^ ((a ^ z) & m)), stage + inst * 1024);
+  }
+}
+
+// Load one page of sequence b into `stage`. Page ids outside the cache or past
+// the block table become zero pages and set the device error word. The page
+// id is read once per wave (it is the same for every lane).
+template <int NW>
+__device__ __forceinline__ void load_page(const DecodeParams& P, int b, int page, int L,
+                                          MLA_LDS char* stage, int wave, int lane) {
+  const bool in_table = page < P.max_blocks;
+  long long pid = 0;
+  if (in_table) pid = __builtin_amdgcn_readfirstlane(P.block_table[(long long)b * P.max_blocks + page]);
+  const bool ok = in_table && pid >= 0 && pid < P.num_pages;
+  if (!ok) flag_error(in_table ? MLA_DEVERR_PAGE_ID : MLA_DEVERR_SEQ_TOO_LONG);
+  const int nvalid = min(kPage, L - page * kPage);
+  const char* base = reinterpret_cast<const char*>(P.kv) + (ok ? pid : 0) * (long long)(kPage * kRowBytes);
+  issue_page<NW>(base, ok, nvalid, stage, wave, lane);
+}
+
+// Divergence note: the kernel keeps every branch wave-uniform. Register
+// pressure makes the compiler park live values (row index, pointers) in spare
+// registers around the epilogue, and a reload placed inside a lane-masked
+// region restores only the active lanes; with no lane-masked regions every
+// reload covers the whole wave. Padding rows are handled by bounds-checked
+// buffer stores and source selects instead of branches.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_kernel(DecodeParams P) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  // restart requests, rotating over three slots: page iteration k writes
+  // slot k % 3, every wave reads it after the next barrier, and slot
+  // (k + 1) % 3 is cleared then (all reads of it finished one barrier earlier,
+  // its next writer starts one barrier later), so all waves see one value
+  __shared__ int restart_flags[3];
+  MLA_LDS char* lds = (MLA_LDS char*)(smem);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id_uniform();
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+
+  // workgroup -> (slot, row block); the row blocks of one slot share an XCD
+  int slot, rb;
+  {
+    const int R = P.n_rowblocks;
+    const int bid = blockIdx.x;
+    if (R == 1) {
+      slot = bid;
+      rb = 0;
+    } else {
+      const int xcd = bid & 7, idx = bid >> 3;
+      slot = (idx / R) * 8 + xcd;
+      rb = idx % R;
+    }
+  }
+  if (slot >= P.num_slots) return;
+  const int* meta = P.tile_meta + slot * MLA_META_WORDS;
+  const int b_begin = meta[0], page_begin = meta[1], b_end = meta[2], page_end = meta[3];
+  const int split_begin = meta[4];
+  if (b_end < b_begin) return;
+
+  const int M = P.M;
+  const int row = rb * (NW * 32) + wave * 32 + r32;  // query row within the sequence
+  const bool row_ok = row < M;
+  const int row_c = min(row, M - 1);                 // padding rows alias the last row (never stored)
+  const int qj = row_c >> P.log2_h;                  // query token index of this row (h is a power of 2)
+  const unsigned keep = row_ok ? 0xffffffffu : 0u;
+  const bf16x8 zero8 = bf16x8{};
+
+  // LDS-relative constants of this lane
+  const int a_off = r32 * kLdsRowStride + g * 16;   // K fragment: token r32, chunk 2*ks + g
+  const int j16 = lane & 15;
+  const int v_off = (4 * g + (j16 >> 2)) * kLdsRowStride + (16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
+
+  for (int b = b_begin; b <= b_end; ++b) {
+    const int L = P.seqlens[b];
+    const int npages = L > 0 ? (L + kPage - 1) / kPage : 0;
+    const int p_lo = (b == b_begin) ? page_begin : 0;
+    const int p_hi = (b == b_end) ? page_end : npages;
+    if (p_hi <= p_lo) continue;
+    const int ns0 = P.num_splits[b], ns1 = P.num_splits[b + 1];
+    const int split = (b == b_begin) ? split_begin : ns0;
+    const bool single = (ns1 - ns0) == 1;
+    const int n_row = P.causal ? L - P.s_q + 1 + qj : L;  // keys this row sees
+    const int n_min = P.causal ? L - P.s_q + 1 : L;       // fewest keys of any row
+    const bool use_lo = P.q_lat_lo != nullptr && L <= MLA_LO_PASS_MAX_LEN;
+
+    const long long qrow = (long long)b * M + row_c;
+    bf16x8 qf[36];
+    {
+      const u32x4* ql = reinterpret_cast<const u32x4*>(P.q_lat + qrow * kDLat) + g;
+      const u32x4* qp = reinterpret_cast<const u32x4*>(P.q_pe + qrow * kDRope) + g;
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) qf[ks] = as_bf16x8(ql[2 * ks] & keep);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = as_bf16x8(qp[2 * ks] & keep);
+    }
+
+    // Softmax reference. Probabilities are exp2(x - m_ref) with m_ref fixed
+    // for the whole piece, so the accumulators never need rescaling; m_ref is
+    // the row's first finite tile max. If a later score exceeds it by more
+    // than kRefSlack (where fp32 sums could start to overflow), the whole
+    // workgroup restarts the piece with the largest max seen so far.
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    f32x16 acc[16];
+    for (;;) {  // restart loop: runs once unless a score outgrows m_ref
+      __syncthreads();  // every wave is done with both page buffers and the flags
+      restart_flags[0] = restart_flags[1] = restart_flags[2] = 0;  // every lane writes 0
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) mfma32_agpr_zero(acc[dt], zero8);
+      m_ref = m_seen;
+      l_run = 0.f;
+      load_page<NW>(P, b, p_lo, L, lds, wave, lane);
+      bool restart = false;
+      for (int p = p_lo, k = 0; p < p_hi; ++p, ++k) {
+        wait_vmem_all();
+        __syncthreads();
+        if (k > 0 && restart_flags[(k + 2) % 3]) { restart = true; break; }  // slot of page k - 1
+        restart_flags[(k + 1) % 3] = 0;
+        MLA_LDS char* cur = lds + (k & 1) * kStageBytes;
+        if (p + 1 < p_hi) load_page<NW>(P, b, p + 1, L, lds + ((k + 1) & 1) * kStageBytes, wave, lane);
+
+#pragma unroll 1
+        for (int tt = 0; tt < 2; ++tt) {
+          MLA_LDS char* tile = cur + tt * 32 * kLdsRowStride;
+          // ---- S^T = K Q^T (576 deep), one k-step of lookahead ----
+          f32x16 sc = f32x16{};
+          {
+            bf16x8 k0 = lds_read16(tile, a_off);
+#pragma unroll
+            for (int ks = 0; ks < 36; ++ks) {
+              bf16x8 n0 = k0;
+              if (ks + 1 < 36) n0 = lds_read16(tile, a_off + (ks + 1) * 32);
+              sc = mfma32(k0, qf[ks], sc);
+              __builtin_amdgcn_sched_barrier(0);
+              k0 = n0;
+            }
+          }
+          if (use_lo) {
+            const u32x4* qlo = reinterpret_cast<const u32x4*>(P.q_lat_lo + qrow * kDLat) + g;
+#pragma unroll 1
+            for (int ks = 0; ks < 32; ++ks)
+              sc = mfma32(lds_read16(tile, a_off + ks * 32), as_bf16x8(qlo[2 * ks] & keep), sc);
+          }
+
+          // ---- softmax numerators, base 2 ----
+          // sc element v is token p*64 + tt*32 + 8*(v/4) + 4*g + v%4
+          const int t0 = p * kPage + tt * 32 + 4 * g;
+          if (p * kPage + tt * 32 + 32 > n_min) {  // some token of this tile is masked for some row
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (t0 + 8 * (v >> 2) + (v & 3) >= n_row) sc[v] = -INFINITY;
+          }
+          float mx = sc[0];
+#pragma unroll
+          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * P.scale_log2e;  // scale > 0 commutes with max
+          m_seen = fmaxf(m_seen, mx);
+          if (m_ref == -INFINITY) m_ref = mx;  // nothing accumulated yet for this row
+          if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRefSlack) != 0ull) restart_flags[k % 3] = 1;
+          const float msub = m_ref == -INFINITY ? 0.f : m_ref;
+          float psum = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            sc[v] = fast_exp2(sc[v] * P.scale_log2e - msub);
+            psum += sc[v];
+          }
+          l_run += psum;
+          const bf16x8 pb0 = pack8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
+          const bf16x8 pb1 = pack8(sc[8], sc[9], sc[10], sc[11], sc[12], sc[13], sc[14], sc[15]);
+
+          // ---- O^T += V^T P^T over this tile's 32 tokens ----
+          {
+            bf16x4 c0 = lds_read_tr4(tile, v_off);
+            bf16x4 c1 = lds_read_tr4(tile, v_off + 8 * kLdsRowStride);
+#pragma unroll
+            for (int it = 0; it < 32; ++it) {  // it = dt * 2 + k-step (tokens 16k .. 16k+15)
+              const int dt = it >> 1, kk = it & 1;
+              bf16x4 n0 = c0, n1 = c1;
+              if (it + 1 < 32) {
+                const int off = v_off + 16 * ((it + 1) & 1) * kLdsRowStride + ((it + 1) >> 1) * 64;
+                n0 = lds_read_tr4(tile, off);
+                n1 = lds_read_tr4(tile, off + 8 * kLdsRowStride);
+              }
+              mfma32_agpr(acc[dt], cat4(c0, c1), kk ? pb1 : pb0);
+              __builtin_amdgcn_sched_barrier(0);
+              c0 = n0;
+              c1 = n1;
+            }
+          }
+        }
+      }
+      if (!restart) {
+        wait_vmem_all();
+        __syncthreads();
+        restart = restart_flags[(p_hi - p_lo - 1) % 3] != 0;
+      }
+      if (!restart) break;
+      wait_vmem_all();  // a restart may leave the next page's loads in flight
+    }
+    mfma_drain();
+
+    // ---- finalise this piece ----
+    // Stores go through buffer resources sized to the valid rows of this row
+    // block: lanes of padding rows get offsets past the end and the hardware
+    // drops their writes, so no lane is masked off by a branch.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_v = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    const int row0 = rb * (NW * 32);                  // first row of this row block
+    const int nrows = min(NW * 32, M - row0);         // valid rows in it
+    const int lrow = wave * 32 + r32;                 // this lane's row within the block
+    if (single) {
+      const long long rbase = (long long)b * M + row0;
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          P.o_lat + rbase * kDLat, 0, nrows * kDLat * 2, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(P.lse + rbase, 0, nrows * 4,
+                                                                          kBufferWord3);
+      const int off = lrow * kDLat * 2 + 8 * g;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          bf16x4 w;
+          w[0] = (__bf16)(acc[dt][4 * vq + 0] * inv_l);
+          w[1] = (__bf16)(acc[dt][4 * vq + 1] * inv_l);
+          w[2] = (__bf16)(acc[dt][4 * vq + 2] * inv_l);
+          w[3] = (__bf16)(acc[dt][4 * vq + 3] * inv_l);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), ro, off + (dt * 32 + 8 * vq) * 2,
+                                                0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
+    } else {
+      const long long pbase = (long long)split * M + row0;
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          P.part_o + pbase * kDLat, 0, nrows * kDLat * 4, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(P.part_lse + pbase, 0, nrows * 4,
+                                                                          kBufferWord3);
+      const int off = lrow * kDLat * 4 + 16 * g;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          u32x4 w;
+          w[0] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 0] * inv_l);
+          w[1] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 1] * inv_l);
+          w[2] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 2] * inv_l);
+          w[3] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 3] * inv_l);
+          __builtin_amdgcn_raw_buffer_store_b128(w, ro, off + (dt * 32 + 8 * vq) * 4, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
+    }
+  }
+}
+
+// Merge split partials: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k.
+// One workgroup per (sequence, 8 rows); 32 threads per row, 16 values each.
+__global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
+  const int b = blockIdx.x;
+  const int row = blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int t = threadIdx.x & 31;
+  if (row >= P.M) return;
+  const int ns0 = P.num_splits[b], n = P.num_splits[b + 1] - ns0;
+  if (n == 1) return;
+  const long long orow = (long long)b * P.M + row;
+  uint16_t* out = P.o_lat + orow * kDLat;
+  if (n == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint2 z = {0u, 0u};
+      *reinterpret_cast<uint2*>(out + 128 * q + 4 * t) = z;
+    }
+    if (t == 0) P.lse[orow] = -INFINITY;
+    return;
+  }
+  float mx = -INFINITY;
+  for (int k = 0; k < n; ++k) mx = fmaxf(mx, P.part_lse[(long long)(ns0 + k) * P.M + row]);
+  f32x4 o[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    for (int k = 0; k < n; ++k) {
+      const long long prow = (long long)(ns0 + k) * P.M + row;
+      const float lk = P.part_lse[prow];
+      const float w = fast_exp2((lk - mx) * 1.4426950408889634f);
+      wsum += w;
+      const f32x4* src = reinterpret_cast<const f32x4*>(P.part_o + prow * kDLat) + t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] += w * src[32 * q];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    bf16x4 w;
+    w[0] = (__bf16)(o[q][0] * inv);
+    w[1] = (__bf16)(o[q][1] * inv);
+    w[2] = (__bf16)(o[q][2] * inv);
+    w[3] = (__bf16)(o[q][3] * inv);
+    *reinterpret_cast<bf16x4*>(out + 128 * q + 4 * t) = w;
+  }
+  if (t == 0) P.lse[orow] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 : -INFINITY;
+}
+
+// The page loader on its own: one workgroup per (page, sequence).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void mla_gather_kernel(DecodeParams P, const long long* row_offsets,
+                                                            uint16_t* out) {
+  __shared__ __attribute__((aligned(16))) char smem[kStageBytes];
+  MLA_LDS char* lds = (MLA_LDS char*)(smem);
+  const int page = blockIdx.x, b = blockIdx.y;
+  const int L = P.seqlens[b];
+  if (page * kPage >= L) return;
+  const int lane = threadIdx.x & 63, wave = wave_id_uniform();
+  load_page<NW>(P, b, page, L, lds, wave, lane);
+  wait_vmem_all();
+  __syncthreads();
+  const int rows = min(kPage, L - page * kPage);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + (row_offsets[b] + (long long)page * kPage) * kDRow);
+  for (int i = threadIdx.x; i < rows * (kRowBytes / 16); i += NW * 64) {
+    const int r = i / (kRowBytes / 16), c = i - r * (kRowBytes / 16);
+    dst[i] = *(const MLA_LDS u32x4*)(lds + r * kLdsRowStride + c * 16);
+  }
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+static int rows_per_wg_waves(int M) { return std::min(4, (M + 31) / 32); }
+
+extern "C" int mla_num_slots(int b, int s_q, int h, int* num_slots) {
+  if (!num_slots) return set_error(MLA_ERR_INVALID_ARG, "mla_num_slots: num_slots is NULL");
+  if (int rc = check_shape("mla_num_slots", b, s_q, h)) return rc;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return set_error(MLA_ERR_HIP, "mla_num_slots: cannot query the device");
+  const int M = s_q * h;
+  const int nw = rows_per_wg_waves(M);
+  const int R = (M + nw * 32 - 1) / (nw * 32);
+  *num_slots = std::max(1, cus / R);
+  return clear_error();
+}
+
+extern "C" size_t mla_workspace_bytes(int b, int s_q, int h, int num_slots) {
+  if (b < 1 || s_q < 1 || h < 1 || num_slots < 1) return 0;
+  const size_t M = (size_t)s_q * h;
+  const size_t splits = (size_t)b + num_slots;
+  const size_t o_bytes = splits * M * kDLat * sizeof(float);
+  const size_t lse_bytes = splits * M * sizeof(float);
+  return ((o_bytes + 255) / 256) * 256 + ((lse_bytes + 255) / 256) * 256;
+}
+
+extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                                const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                int max_blocks, const int32_t* cache_seqlens, int b, int s_q, int h,
+                                float softmax_scale, int causal, const int32_t* tile_meta,
+                                const int32_t* num_splits, int num_slots, void* workspace,
+                                size_t workspace_bytes, uint16_t* o_lat, float* lse, void* stream) {
+  const char* fn = "mla_decode_paged";
+  if (!q_lat || !q_pe || !kv_cache || !block_table || !cache_seqlens || !tile_meta || !num_splits ||
+      !workspace || !o_lat || !lse)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+  if (int rc = check_shape(fn, b, s_q, h)) return rc;
+  if (num_pages < 1 || max_blocks < 1 || num_slots < 1)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: num_pages, max_blocks and num_slots must be >= 1", fn);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return set_error(MLA_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = mla_workspace_bytes(b, s_q, h, num_slots);
+  if (workspace_bytes < need)
+    return set_error(MLA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  for (const void* p : {(const void*)q_lat, (const void*)q_pe, (const void*)kv_cache, (const void*)o_lat})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return set_error(MLA_ERR_INVALID_ARG, "%s: bf16 tensors must be 16-byte aligned", fn);
+  if (q_lat_lo && reinterpret_cast<uintptr_t>(q_lat_lo) % 16 != 0)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: q_lat_lo must be 16-byte aligned", fn);
+
+  const int M = s_q * h;
+  const int nw = rows_per_wg_waves(M);
+  const int R = (M + nw * 32 - 1) / (nw * 32);
+  const size_t M_ = (size_t)M, splits = (size_t)b + num_slots;
+  char* ws = static_cast<char*>(workspace);
+  DecodeParams P;
+  P.q_lat = q_lat;
+  P.q_lat_lo = q_lat_lo;
+  P.q_pe = q_pe;
+  P.kv = kv_cache;
+  P.block_table = block_table;
+  P.seqlens = cache_seqlens;
+  P.tile_meta = tile_meta;
+  P.num_splits = num_splits;
+  P.part_o = reinterpret_cast<float*>(ws);
+  P.part_lse = reinterpret_cast<float*>(ws + ((splits * M_ * kDLat * 4 + 255) / 256) * 256);
+  P.o_lat = o_lat;
+  P.lse = lse;
+  P.num_pages = num_pages;
+  P.max_blocks = max_blocks;
+  P.b = b;
+  P.s_q = s_q;
+  P.h = h;
+  P.log2_h = __builtin_ctz((unsigned)h);
+  P.M = M;
+  P.n_rowblocks = R;
+  P.num_slots = num_slots;
+  P.causal = causal ? 1 : 0;
+  P.scale_log2e = softmax_scale * 1.4426950408889634f;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int grid = R == 1 ? num_slots : ((num_slots + 7) / 8) * 8 * R;
+  switch (nw) {
+    case 1: hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(grid), dim3(64), 0, st, P); break;
+    case 2: hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(grid), dim3(128), 0, st, P); break;
+    default: hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(grid), dim3(256), 0, st, P); break;
+  }
+  if (hipError_t e = hipGetLastError(); e != hipSuccess)
+    return set_error(MLA_ERR_HIP, "%s: decode launch failed: %s", fn, hipGetErrorString(e));
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(b, (M + 7) / 8), dim3(256), 0, st, P);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess)
+    return set_error(MLA_ERR_HIP, "%s: combine launch failed: %s", fn, hipGetErrorString(e));
+  return clear_error();
+}
+
+extern "C" int mla_gather_pages(const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                int max_blocks, const int32_t* cache_seqlens, int b,
+                                const int64_t* row_offsets, uint16_t* out, void* stream) {
+  const char* fn = "mla_gather_pages";
+  if (!kv_cache || !block_table || !cache_seqlens || !row_offsets || !out)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+  if (b < 1 || num_pages < 1 || max_blocks < 1)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: b, num_pages and max_blocks must be >= 1", fn);
+  if (reinterpret_cast<uintptr_t>(kv_cache) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: kv_cache and out must be 16-byte aligned", fn);
+  DecodeParams P{};
+  P.kv = kv_cache;
+  P.block_table = block_table;
+  P.seqlens = cache_seqlens;
+  P.num_pages = num_pages;
+  P.max_blocks = max_blocks;
+  P.b = b;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // one wave and four waves take different shares of the same load pattern
+  hipLaunchKernelGGL(mla_gather_kernel<4>, dim3(max_blocks, b), dim3(256), 0, st, P,
+                     reinterpret_cast<const long long*>(row_offsets), out);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess)
+    return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return clear_error();
+}
+
+extern "C" int mla_take_device_error(int* bits) {
+  if (!bits) return set_error(MLA_ERR_INVALID_ARG, "mla_take_device_error: bits is NULL");
+  int v = 0, zero = 0;
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_device_error), sizeof(int), 0, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(g_device_error), &zero, sizeof(int), 0, hipMemcpyHostToDevice) != hipSuccess)
+    return set_error(MLA_ERR_HIP, "mla_take_device_error: cannot read the device error word");
+  *bits = v;
+  return clear_error();
+}

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every function include/mla.h declares, and
+rejects bad arguments on the host before anything is launched (no GPU needed).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+LIB = os.path.join(ROOT, "mla_decode_paged_amd", "libmla.so")
+
+MLA_OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        subprocess.run(["python", "-m", "mla_decode_paged_amd.build"], cwd=ROOT, check=True)
+    import mla_decode_paged_amd as mla
+    return mla.load()
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for fn in ("mla_get_metadata", "mla_absorb_q", "mla_decode_paged", "mla_up_v", "mla_gather_pages",
+               "mla_last_error", "mla_num_slots", "mla_workspace_bytes", "mla_take_device_error"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (mla_\w+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    for f in declared_functions():
+        getattr(lib, f)
+
+
+def test_workspace_formula(lib):
+    # fp32 partials [b + slots, M, 512] and lse [b + slots, M], each padded to 256 bytes
+    b, s_q, h, slots = 128, 1, 128, 256
+    M = s_q * h
+    o = (b + slots) * M * 512 * 4
+    l = (b + slots) * M * 4
+    pad = lambda x: (x + 255) // 256 * 256
+    assert lib.mla_workspace_bytes(b, s_q, h, slots) == pad(o) + pad(l)
+    assert lib.mla_workspace_bytes(0, 1, 128, 8) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every case fails validation first
+
+
+def _decode(lib, **kw):
+    a = dict(q_lat=FAKE, q_lat_lo=None, q_pe=FAKE, kv=FAKE, num_pages=10, bt=FAKE, max_blocks=4, sl=FAKE, b=2,
+             s_q=1, h=16, scale=0.07, causal=0, meta=FAKE, ns=FAKE, slots=8, ws=FAKE, ws_bytes=1 << 30, o=FAKE,
+             lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_paged(a["q_lat"], a["q_lat_lo"], a["q_pe"], a["kv"], a["num_pages"], a["bt"],
+                                a["max_blocks"], a["sl"], a["b"], a["s_q"], a["h"], a["scale"], a["causal"],
+                                a["meta"], a["ns"], a["slots"], a["ws"], a["ws_bytes"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q_lat=None), INVALID, "NULL"),
+    (dict(kv=None), INVALID, "NULL"),
+    (dict(b=0), INVALID, "b must be"),
+    (dict(s_q=9), INVALID, "s_q"),
+    (dict(h=48), UNSUPPORTED, "h must be"),
+    (dict(scale=0.0), INVALID, "softmax_scale"),
+    (dict(scale=float("nan")), INVALID, "softmax_scale"),
+    (dict(num_pages=0), INVALID, "num_pages"),
+    (dict(slots=0), INVALID, "num_slots"),
+    (dict(ws_bytes=1000), WORKSPACE, "workspace"),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16)), INVALID, "aligned"),
+    (dict(q_lat=ctypes.c_void_p((1 << 20) + 2)), INVALID, "aligned"),
+])
+def test_decode_rejects(lib, kw, code, msg):
+    assert _decode(lib, **kw) == code
+    assert msg in lib.mla_last_error().decode()
+
+
+def test_other_calls_reject(lib):
+    assert lib.mla_get_metadata(FAKE, 0, 8, 2, FAKE, FAKE, None) == INVALID
+    assert lib.mla_get_metadata(FAKE, 9000, 8, 2, FAKE, FAKE, None) == INVALID
+    assert lib.mla_get_metadata(FAKE, 4, 0, 2, FAKE, FAKE, None) == INVALID
+    assert lib.mla_get_metadata(FAKE, 4, 8, -1, FAKE, FAKE, None) == INVALID
+    assert lib.mla_get_metadata(None, 4, 8, 2, FAKE, FAKE, None) == INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, None, 2, 1, 100, None) == UNSUPPORTED
+    assert lib.mla_absorb_q(None, FAKE, FAKE, None, 2, 1, 16, None) == INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 8), 2, 1, 16, None) == INVALID
+    assert lib.mla_up_v(FAKE, FAKE, None, 2, 1, 16, None) == INVALID
+    assert lib.mla_up_v(FAKE, FAKE, FAKE, 2, 0, 16, None) == INVALID
+    assert lib.mla_gather_pages(FAKE, 0, FAKE, 4, FAKE, 2, FAKE, FAKE, None) == INVALID
+    assert lib.mla_gather_pages(FAKE, 4, FAKE, 4, FAKE, 2, None, FAKE, None) == INVALID
+    assert lib.mla_num_slots(2, 1, 16, None) == INVALID
+    assert lib.mla_take_device_error(None) == INVALID
+    assert lib.mla_last_error().decode() != ""
