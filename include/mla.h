@@ -54,10 +54,6 @@ extern "C" {
 #define MLA_D_ROPE 64
 #define MLA_D_ROW 576
 #define MLA_D_NOPE 128
-/* Sequences no longer than this score the bf16 lo plane of q_lat as well
- * (when one is passed): bf16 rounding of q_lat alone moves lse by up to
- * ~5e-3 on very short caches. */
-#define MLA_LO_PASS_MAX_LEN 1024
 /* int32 words per slot in tile_meta */
 #define MLA_META_WORDS 8
 /* Largest batch the planner accepts. */
@@ -130,8 +126,10 @@ int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_lat, 
  * Token t of sequence b is row t % 64 of page block_table[b, t / 64].
  * With causal != 0, query j sees the first L_b - s_q + 1 + j tokens;
  * otherwise all L_b. A row that sees no token gets o_lat = 0, lse = -inf.
- * When q_lat_lo is given, sequences with L_b <= MLA_LO_PASS_MAX_LEN add
- * q_lat_lo . c_t to the score.
+ * Scores use bf16 q_lat. When q_lat_lo (the bf16 rounding residue from
+ * mla_absorb_q) is given, lse also carries that residue's first-order effect,
+ * softmax_scale * (q_lat_lo[r] . o_lat[r]) (d lse / d s_t = p_t): without it
+ * the bf16 rounding of q_lat alone moves lse by up to ~5e-3 on short caches.
  *
  * q_lat, q_lat_lo  bf16 [b, s_q, h, 512] (lo nullable), from mla_absorb_q
  * q_pe             bf16 [b, s_q, h, 64], rotated

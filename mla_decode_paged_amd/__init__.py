@@ -25,11 +25,10 @@ import torch
 
 __all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "decode_paged",
            "up_v", "gather_pages", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
-           "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE", "LO_PASS_MAX_LEN"]
+           "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 PAGE_TOKENS, D_LATENT, D_ROPE, D_ROW, D_NOPE = 64, 512, 64, 576, 128
-LO_PASS_MAX_LEN = 1024
 META_WORDS = 8
 # fixed cost of one sequence piece in the split plan, in pages
 SPLIT_OVERHEAD = 2

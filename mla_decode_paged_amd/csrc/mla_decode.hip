@@ -10,13 +10,19 @@
 // How it maps onto MI355X (one workgroup = NW wavefronts, 32 query rows each):
 //  * Page loader. A page is 64 rows x 1152 contiguous bytes. It is copied
 //    straight from HBM into LDS with 16-byte direct-to-LDS loads
-//    (global_load_lds_dwordx4): 73 wave instructions of 1 KB each cover the
-//    64 rows at a padded LDS row stride of 1168 bytes (the 73rd 16-byte slot of
-//    each LDS row is padding). Two page buffers alternate, so the next page
-//    streams in while the current one is multiplied; this is the double
-//    buffer of the SC11 note's Page Attention figure, done by the CU's own
-//    load path instead of separate DMA engines. Tokens past the cache length
-//    and bad page ids load a zero row, so NaN or stale data never reach LDS.
+//    (global_load_lds_dwordx4), one wave instruction per 8-row x 128-byte
+//    block: 72 instructions per page. Each lane of every instruction reads the
+//    same in-block position, so its source address is a per-lane constant
+//    plus a per-instruction scalar offset and the loader costs no vector ALU
+//    work. Inside a block the 16-byte chunks of row r are XOR-permuted and
+//    each 8-row block row is shifted by 32 bytes; with that, the K-fragment
+//    reads of QK^T (32 rows x 16 bytes) and the transposed V reads of PV
+//    (4 rows x 32 bytes per 16 lanes) both hit 64 distinct banks. Two page
+//    buffers alternate, so the next page streams in while the current one is
+//    multiplied; this is the double buffer of the SC11 note's Page Attention
+//    figure, done by the CU's own load path instead of separate DMA engines.
+//    Tokens past the cache length and bad page ids load a zero row, so NaN or
+//    stale data never reach LDS.
 //  * QK^T on the matrix cores, transposed: S^T[token, row] = K Q^T with K
 //    (the page rows) as the A operand read from LDS and Q as the B operand
 //    held in VGPRs for the whole piece. Each lane then owns 16 scores of ONE
@@ -49,15 +55,24 @@ namespace mla {
 __device__ int g_device_error = 0;
 __device__ const uint4 g_zero_row[kRowBytes / 16] = {};
 
-constexpr int kLdsRowStride = kRowBytes + 16;              // 1168
-constexpr int kLdsSlotsPerRow = kLdsRowStride / 16;         // 73
-constexpr int kStageBytes = kPage * kLdsRowStride;          // 74752
-constexpr int kLoadInstrPerPage = kPage * kLdsSlotsPerRow / 64;  // 73
+// LDS page layout (bytes): block (rb, cb) = rows 8rb..8rb+7, chunks 8cb..8cb+7
+// sits at rb * kBlkRowStride + cb * 1024; inside it, row r's chunk c is at
+// (r % 8) * 128 + ((c % 8) ^ swz(r % 8)) * 16.
+constexpr int kBlkBytes = 1024;                              // one wave load instruction
+constexpr int kBlkCols = kRowBytes / 128;                    // 9 blocks per 8 rows
+constexpr int kBlkRowStride = kBlkCols * kBlkBytes + 32;     // 9248: +32 B rotates banks by 8
+constexpr int kStageBytes = (kPage / 8) * kBlkRowStride;     // 73984 per page buffer
+constexpr int kRowsBytes8 = 8 * kRowBytes;                   // 9216: 8 cache rows in HBM
+
+__device__ __forceinline__ int chunk_swz(int lr) { return ((lr >> 1) & 1) * 4 + (lr >> 2); }
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return (r >> 3) * kBlkRowStride + (c >> 3) * kBlkBytes + (r & 7) * 128 + (((c & 7) ^ chunk_swz(r & 7)) << 4);
+}
+
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource: dword data, bounds-checked
 constexpr float kRefSlack = 64.0f;  // log2 units a score may exceed the softmax reference
 
-static_assert(kPage * kLdsSlotsPerRow % 64 == 0, "page must fill whole wave loads");
 
 struct DecodeParams {
   const uint16_t* q_lat;
@@ -74,47 +89,54 @@ struct DecodeParams {
   float* lse;
   long long num_pages;
   int max_blocks, b, s_q, h, log2_h, M, n_rowblocks, num_slots, causal;
-  float scale_log2e;
+  float scale, scale_log2e;
 };
 
 __device__ __forceinline__ void flag_error(int bit) { atomicOr(&g_device_error, bit); }
 
-// Issue this wave's share of the direct-to-LDS loads of one page.
-// nvalid: rows of the page that hold tokens (< 64 on the last page).
-// Every lane runs the same instructions: the source address is chosen by a
-// bit select, never by a branch (see the note on divergence at the kernel).
+// Load one page of sequence b into `stage` with direct-to-LDS loads: wave w
+// copies block rows [w * 8/NW, (w+1) * 8/NW). Lane l always fills in-block
+// position l: row l / 8 and chunk (l % 8) ^ swz(l / 8) of the block, so its
+// HBM address is page + lane_off + (uniform block offset). Page ids outside
+// the cache or past the block table become zero pages and set the device
+// error word; rows past the cache length read the zero row. Every branch is
+// uniform (see the note on divergence at the kernel).
 template <int NW>
-__device__ __forceinline__ void issue_page(const char* page_base, bool page_ok, int nvalid,
-                                           MLA_LDS char* stage, int wave, int lane) {
-  const uintptr_t zero = reinterpret_cast<uintptr_t>(g_zero_row);
-  const uintptr_t base = reinterpret_cast<uintptr_t>(page_base);
-#pragma unroll 1
-  for (int inst = wave; inst < kLoadInstrPerPage; inst += NW) {
-    const int s = inst * 64 + lane;
-    const int row = s / kLdsSlotsPerRow;
-    const int c = s - row * kLdsSlotsPerRow;
-    const bool real = page_ok && row < nvalid && c < kLdsSlotsPerRow - 1;
-    const uintptr_t a = base + (uintptr_t)(row * kRowBytes + c * 16);
-    const uintptr_t z = zero + (uintptr_t)((c & 63) * 16);
-    const uintptr_t m = (uintptr_t)0 - (uintptr_t)real;
-    g2lds16(reinterpret_cast<const void*>(z ^ ((a ^ z) & m)), stage + inst * 1024);
-  }
-}
-
-// Load one page of sequence b into `stage`. Page ids outside the cache or past
-// the block table become zero pages and set the device error word. The page
-// id is read once per wave (it is the same for every lane).
-template <int NW>
-__device__ __forceinline__ void load_page(const DecodeParams& P, int b, int page, int L,
-                                          MLA_LDS char* stage, int wave, int lane) {
+__device__ __forceinline__ void load_page(const DecodeParams& P, int b, int page, int L, MLA_LDS char* stage,
+                                          int wave, int lane) {
   const bool in_table = page < P.max_blocks;
   long long pid = 0;
   if (in_table) pid = __builtin_amdgcn_readfirstlane(P.block_table[(long long)b * P.max_blocks + page]);
   const bool ok = in_table && pid >= 0 && pid < P.num_pages;
   if (!ok) flag_error(in_table ? MLA_DEVERR_PAGE_ID : MLA_DEVERR_SEQ_TOO_LONG);
   const int nvalid = min(kPage, L - page * kPage);
-  const char* base = reinterpret_cast<const char*>(P.kv) + (ok ? pid : 0) * (long long)(kPage * kRowBytes);
-  issue_page<NW>(base, ok, nvalid, stage, wave, lane);
+  const char* page_base = reinterpret_cast<const char*>(P.kv) + (ok ? pid : 0) * (long long)(kPage * kRowBytes);
+  const int lr = lane >> 3, lc = (lane & 7) ^ chunk_swz(lane >> 3);
+  const int lane_off = lr * kRowBytes + lc * 16;
+  constexpr int kRB = 8 / NW;  // block rows per wave
+  if (ok && nvalid == kPage) {
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      const int rb = wave * kRB + i;
+      const char* src = page_base + rb * kRowsBytes8 + lane_off;
+      MLA_LDS char* dst = stage + rb * kBlkRowStride;
+#pragma unroll
+      for (int cb = 0; cb < kBlkCols; ++cb) g2lds16(src + cb * 128, dst + cb * kBlkBytes);
+    }
+  } else {  // last page of a sequence, or a bad page id: pick rows by a bit select
+    const uintptr_t zero = reinterpret_cast<uintptr_t>(g_zero_row) + lc * 16;
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      const int rb = wave * kRB + i;
+      const uintptr_t real = reinterpret_cast<uintptr_t>(page_base + rb * kRowsBytes8 + lane_off);
+      const uintptr_t m = (uintptr_t)0 - (uintptr_t)(ok && rb * 8 + lr < nvalid);
+      const uintptr_t src = zero ^ ((real ^ zero) & m);
+      MLA_LDS char* dst = stage + rb * kBlkRowStride;
+#pragma unroll
+      for (int cb = 0; cb < kBlkCols; ++cb)
+        g2lds16(reinterpret_cast<const void*>(src + (uintptr_t)(cb * 128)), dst + cb * kBlkBytes);
+    }
+  }
 }
 
 // Divergence note: the kernel keeps every branch wave-uniform. Register
@@ -167,10 +189,29 @@ void mla_decode_kernel(DecodeParams P) {
   const unsigned keep = row_ok ? 0xffffffffu : 0u;
   const bf16x8 zero8 = bf16x8{};
 
-  // LDS-relative constants of this lane
-  const int a_off = r32 * kLdsRowStride + g * 16;   // K fragment: token r32, chunk 2*ks + g
-  const int j16 = lane & 15;
-  const int v_off = (4 * g + (j16 >> 2)) * kLdsRowStride + (16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
+  // LDS-relative constants of this lane (see the layout at kBlkRowStride).
+  // K fragment for k-step ks of a 32-token tile: token r32, chunk 2 ks + g
+  //   -> a_base[ks % 4] + (ks / 4) * 1024.
+  int a_base[4];
+  {
+    const int lr = r32 & 7;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+      a_base[k4] = (r32 >> 3) * kBlkRowStride + lr * 128 + (((2 * k4 + g) ^ chunk_swz(lr)) << 4);
+  }
+  // V^T fragment (transposed read) for d-tile dt and k-step kk of a tile:
+  //   rows 16 kk + 4 g + j/4 (+8 for the second read), byte column
+  //   64 dt + 32 ((lane/16) & 1) + 8 (j & 3)
+  //   -> v_base[dt % 2] + (dt / 2) * 1024 + 2 kk * kBlkRowStride (+ kBlkRowStride).
+  int v_base[2];
+  {
+    const int j16 = lane & 15;
+    const int lr = 4 * g + (j16 >> 2);
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2)
+      v_base[p2] = lr * 128 + (((4 * p2 + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1)) ^ chunk_swz(lr)) << 4) +
+                   8 * (j16 & 1);
+  }
 
   for (int b = b_begin; b <= b_end; ++b) {
     const int L = P.seqlens[b];
@@ -183,7 +224,6 @@ void mla_decode_kernel(DecodeParams P) {
     const bool single = (ns1 - ns0) == 1;
     const int n_row = P.causal ? L - P.s_q + 1 + qj : L;  // keys this row sees
     const int n_min = P.causal ? L - P.s_q + 1 : L;       // fewest keys of any row
-    const bool use_lo = P.q_lat_lo != nullptr && L <= MLA_LO_PASS_MAX_LEN;
 
     const long long qrow = (long long)b * M + row_c;
     bf16x8 qf[36];
@@ -222,25 +262,21 @@ void mla_decode_kernel(DecodeParams P) {
 
 #pragma unroll 1
         for (int tt = 0; tt < 2; ++tt) {
-          MLA_LDS char* tile = cur + tt * 32 * kLdsRowStride;
-          // ---- S^T = K Q^T (576 deep), one k-step of lookahead ----
+          MLA_LDS char* tile = cur + tt * 4 * kBlkRowStride;
+          // ---- S^T = K Q^T (576 deep), fragments read four k-steps ahead ----
+          // the sched barriers keep the scheduler from hoisting every fragment
+          // read (they would not fit in VGPRs)
           f32x16 sc = f32x16{};
           {
-            bf16x8 k0 = lds_read16(tile, a_off);
+            bf16x8 kr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kr[i] = lds_read16(tile, a_base[i]);
 #pragma unroll
             for (int ks = 0; ks < 36; ++ks) {
-              bf16x8 n0 = k0;
-              if (ks + 1 < 36) n0 = lds_read16(tile, a_off + (ks + 1) * 32);
-              sc = mfma32(k0, qf[ks], sc);
+              sc = mfma32(kr[ks & 3], qf[ks], sc);
+              if (ks + 4 < 36) kr[ks & 3] = lds_read16(tile, a_base[(ks + 4) & 3] + ((ks + 4) >> 2) * kBlkBytes);
               __builtin_amdgcn_sched_barrier(0);
-              k0 = n0;
             }
-          }
-          if (use_lo) {
-            const u32x4* qlo = reinterpret_cast<const u32x4*>(P.q_lat_lo + qrow * kDLat) + g;
-#pragma unroll 1
-            for (int ks = 0; ks < 32; ++ks)
-              sc = mfma32(lds_read16(tile, a_off + ks * 32), as_bf16x8(qlo[2 * ks] & keep), sc);
           }
 
           // ---- softmax numerators, base 2 ----
@@ -269,23 +305,26 @@ void mla_decode_kernel(DecodeParams P) {
           const bf16x8 pb0 = pack8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
           const bf16x8 pb1 = pack8(sc[8], sc[9], sc[10], sc[11], sc[12], sc[13], sc[14], sc[15]);
 
-          // ---- O^T += V^T P^T over this tile's 32 tokens ----
+          // ---- O^T += V^T P^T over this tile's 32 tokens, fragments four steps ahead ----
           {
-            bf16x4 c0 = lds_read_tr4(tile, v_off);
-            bf16x4 c1 = lds_read_tr4(tile, v_off + 8 * kLdsRowStride);
+            bf16x4 vr[4][2];
 #pragma unroll
-            for (int it = 0; it < 32; ++it) {  // it = dt * 2 + k-step (tokens 16k .. 16k+15)
+            for (int i = 0; i < 4; ++i) {  // step it = dt * 2 + kk
+              const int o = v_base[(i >> 1) & 1] + ((i >> 1) >> 1) * kBlkBytes + 2 * (i & 1) * kBlkRowStride;
+              vr[i][0] = lds_read_tr4(tile, o);
+              vr[i][1] = lds_read_tr4(tile, o + kBlkRowStride);
+            }
+#pragma unroll
+            for (int it = 0; it < 32; ++it) {
               const int dt = it >> 1, kk = it & 1;
-              bf16x4 n0 = c0, n1 = c1;
-              if (it + 1 < 32) {
-                const int off = v_off + 16 * ((it + 1) & 1) * kLdsRowStride + ((it + 1) >> 1) * 64;
-                n0 = lds_read_tr4(tile, off);
-                n1 = lds_read_tr4(tile, off + 8 * kLdsRowStride);
+              mfma32_agpr(acc[dt], cat4(vr[it & 3][0], vr[it & 3][1]), kk ? pb1 : pb0);
+              if (it + 4 < 32) {
+                const int n = it + 4, ndt = n >> 1;
+                const int o = v_base[ndt & 1] + (ndt >> 1) * kBlkBytes + 2 * (n & 1) * kBlkRowStride;
+                vr[it & 3][0] = lds_read_tr4(tile, o);
+                vr[it & 3][1] = lds_read_tr4(tile, o + kBlkRowStride);
               }
-              mfma32_agpr(acc[dt], cat4(c0, c1), kk ? pb1 : pb0);
               __builtin_amdgcn_sched_barrier(0);
-              c0 = n0;
-              c1 = n1;
             }
           }
         }
@@ -306,7 +345,30 @@ void mla_decode_kernel(DecodeParams P) {
     // drops their writes, so no lane is masked off by a branch.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    float lse_v = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    if (P.q_lat_lo != nullptr) {
+      // The scores used q_lat rounded to bf16; the residue q_lo = q_lat - bf16(q_lat)
+      // shifts score t by scale * (q_lo . c_t). lse is smooth in the scores with
+      // d lse / d s_t = p_t, so to first order lse moves by
+      // scale * sum_t p_t (q_lo . c_t) = scale * (q_lo . o_lat): one 512-long dot
+      // per row instead of a second pass over every token. The dropped second
+      // order term is at most half the square of the largest shift (~1e-5).
+      const uint2* qlo = reinterpret_cast<const uint2*>(P.q_lat_lo + qrow * kDLat + 4 * g);
+      uint2 qv[64];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) qv[i] = qlo[(i >> 2) * 8 + (i & 3) * 2];  // d = 32 dt + 8 vq + 4 g
+      float dot = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const bf16x4 q4 = __builtin_bit_cast(bf16x4, qv[dt * 4 + vq]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot += acc[dt][4 * vq + e] * (float)q4[e];
+        }
+      dot += __shfl_xor(dot, 32);
+      if (l_tot > 0.f) lse_v += P.scale * dot * inv_l;
+    }
     const int row0 = rb * (NW * 32);                  // first row of this row block
     const int nrows = min(NW * 32, M - row0);         // valid rows in it
     const int lrow = wave * 32 + r32;                 // this lane's row within the block
@@ -420,7 +482,7 @@ __global__ __launch_bounds__(NW * 64) void mla_gather_kernel(DecodeParams P, con
   u32x4* dst = reinterpret_cast<u32x4*>(out + (row_offsets[b] + (long long)page * kPage) * kDRow);
   for (int i = threadIdx.x; i < rows * (kRowBytes / 16); i += NW * 64) {
     const int r = i / (kRowBytes / 16), c = i - r * (kRowBytes / 16);
-    dst[i] = *(const MLA_LDS u32x4*)(lds + r * kLdsRowStride + c * 16);
+    dst[i] = *(const MLA_LDS u32x4*)(lds + lds_off(r, c));
   }
 }
 
@@ -507,6 +569,7 @@ extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo,
   P.n_rowblocks = R;
   P.num_slots = num_slots;
   P.causal = causal ? 1 : 0;
+  P.scale = softmax_scale;
   P.scale_log2e = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -55,25 +55,22 @@ def test_causal_row0_equals_shorter_decode(gpu_lib):
     inp1.q_pe = np.ascontiguousarray(inp2.q_pe[:, :1])
     inp1.seqlens = inp2.seqlens - 1
     r1 = host(run_path(gpu_lib, DevInputs(inp1)))
-    # the lo pass threshold compares the cache length, which differs by one here (1025 vs 1024)
-    keep = [0, 2]
-    assert np.array_equal(r2["lse"][keep, 0], r1["lse"][keep, 0])
-    assert np.array_equal(r2["o_lat"][keep, 0], r1["o_lat"][keep, 0])
+    # both plans cut the same pages, so row 0 is computed in the same order: bit-identical
+    assert np.array_equal(r2["lse"][:, 0], r1["lse"][:, 0])
+    assert np.array_equal(r2["o_lat"][:, 0], r1["o_lat"][:, 0])
 
 
 def test_large_score_growth_restarts_exactly(gpu_lib):
     """A key scoring far above the first tile's max forces a recompute with a
-    larger softmax reference; the result still matches the oracle.
-
-    Both caches stay within the lo-pass length: with attention on one token,
-    lse inherits that one score's error, and bf16 q_lat alone (no lo plane)
-    leaves about 1e-3 there."""
-    inp = make_inputs("tiny", seed=9, seqlens=[300, 1000], h=16)
+    larger softmax reference; the result still matches the oracle (with the
+    attention on one token, lse carries that one score's error: the lo-plane
+    correction removes it)."""
+    inp = make_inputs("tiny", seed=9, seqlens=[300, 2100], h=16)
     # make one late token of each sequence dominate: scale its positional key
     # up (its latent values, which form the output, stay ordinary)
     from mla_inputs import bf16_bits, f32
     kv = f32(inp.kv_cache)
-    for b, t in ((0, 250), (1, 990)):
+    for b, t in ((0, 250), (1, 2000)):
         pg, sl = inp.block_table[b, t // 64], t % 64
         kv[pg, sl, 512:] *= 80.0
     inp.kv_cache = bf16_bits(kv)

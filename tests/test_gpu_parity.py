@@ -37,7 +37,7 @@ def test_tiny_config_poisoned(gpu_lib):
     ([1, 2, 3, 64, 65, 200], 2, 16, True),        # causal rows with 0 .. L - 1 keys
     ([0, 7, 0, 100], 1, 32, False),                # empty sequences
     ([300, 1500, 2100], 3, 16, True),              # 48 rows: two-wave workgroups
-    ([130, 1100, 1030], 1, 64, False),             # lo pass on one side of the threshold only
+    ([130, 1100, 1030], 1, 64, False),
     ([1025, 1024, 5], 2, 64, True),
     ([700, 90], 4, 32, True),                      # 128 rows
     ([333, 2000], 4, 128, True),                   # 512 rows: four row blocks
@@ -57,7 +57,7 @@ def test_forced_split_counts(gpu_lib, slots):
 
 
 def test_without_lo_plane_long_rows(gpu_lib):
-    """Past the lo-pass length bf16 q_lat alone meets the bar."""
+    """On long caches with spread-out attention bf16 q_lat alone meets the bar."""
     inp = make_inputs("full_heads", seed=8, seqlens=[1100, 2500, 4096, 3000])
     _check_all(gpu_lib, inp, lo=False)
 
