@@ -63,6 +63,8 @@ constexpr int kBlkCols = kRowBytes / 128;                    // 9 blocks per 8 r
 constexpr int kBlkRowStride = kBlkCols * kBlkBytes + 32;     // 9248: +32 B rotates banks by 8
 constexpr int kStageBytes = (kPage / 8) * kBlkRowStride;     // 73984 per page buffer
 constexpr int kRowsBytes8 = 8 * kRowBytes;                   // 9216: 8 cache rows in HBM
+constexpr int kQloStride = kDLat * 2 + 16;                   // q_lo rows staged in LDS: 1040 B apart
+static_assert(4 * 32 * kQloStride <= 2 * kStageBytes, "q_lo staging must fit in the page buffers");
 
 __device__ __forceinline__ int chunk_swz(int lr) { return ((lr >> 1) & 1) * 4 + (lr >> 2); }
 __device__ __forceinline__ int lds_off(int r, int c) {
@@ -94,6 +96,20 @@ struct DecodeParams {
 
 __device__ __forceinline__ void flag_error(int bit) { atomicOr(&g_device_error, bit); }
 
+// Read-only plan and table data read at wave-uniform addresses go through the
+// scalar cache: nothing in these kernels writes them, so the constant address
+// space is valid for the whole launch.
+__device__ __forceinline__ int ldc(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// Block-table entry of `page` of sequence b (-1 past the table). The kernels
+// read it one page ahead of load_page, so its latency hides behind a page of
+// work instead of stalling the loader.
+__device__ __forceinline__ int fetch_pid(const DecodeParams& P, int b, int page) {
+  return page < P.max_blocks ? P.block_table[(long long)b * P.max_blocks + page] : -1;
+}
+
 // Load one page of sequence b into `stage` with direct-to-LDS loads: wave w
 // copies block rows [w * 8/NW, (w+1) * 8/NW). Lane l always fills in-block
 // position l: row l / 8 and chunk (l % 8) ^ swz(l / 8) of the block, so its
@@ -103,10 +119,9 @@ __device__ __forceinline__ void flag_error(int bit) { atomicOr(&g_device_error, 
 // uniform (see the note on divergence at the kernel).
 template <int NW>
 __device__ __forceinline__ void load_page(const DecodeParams& P, int b, int page, int L, MLA_LDS char* stage,
-                                          int wave, int lane) {
+                                          int wave, int lane, int pid_fetched) {
   const bool in_table = page < P.max_blocks;
-  long long pid = 0;
-  if (in_table) pid = __builtin_amdgcn_readfirstlane(P.block_table[(long long)b * P.max_blocks + page]);
+  const long long pid = __builtin_amdgcn_readfirstlane(pid_fetched);  // from fetch_pid
   const bool ok = in_table && pid >= 0 && pid < P.num_pages;
   if (!ok) flag_error(in_table ? MLA_DEVERR_PAGE_ID : MLA_DEVERR_SEQ_TOO_LONG);
   const int nvalid = min(kPage, L - page * kPage);
@@ -177,8 +192,8 @@ void mla_decode_kernel(DecodeParams P) {
   }
   if (slot >= P.num_slots) return;
   const int* meta = P.tile_meta + slot * MLA_META_WORDS;
-  const int b_begin = meta[0], page_begin = meta[1], b_end = meta[2], page_end = meta[3];
-  const int split_begin = meta[4];
+  const int b_begin = ldc(meta + 0), page_begin = ldc(meta + 1), b_end = ldc(meta + 2), page_end = ldc(meta + 3);
+  const int split_begin = ldc(meta + 4);
   if (b_end < b_begin) return;
 
   const int M = P.M;
@@ -214,12 +229,13 @@ void mla_decode_kernel(DecodeParams P) {
   }
 
   for (int b = b_begin; b <= b_end; ++b) {
-    const int L = P.seqlens[b];
+    const int L = ldc(P.seqlens + b);
     const int npages = L > 0 ? (L + kPage - 1) / kPage : 0;
     const int p_lo = (b == b_begin) ? page_begin : 0;
     const int p_hi = (b == b_end) ? page_end : npages;
     if (p_hi <= p_lo) continue;
-    const int ns0 = P.num_splits[b], ns1 = P.num_splits[b + 1];
+    const int ns0 = ldc(P.num_splits + b), ns1 = ldc(P.num_splits + b + 1);
+    const int pid_first = p_lo < P.max_blocks ? ldc(P.block_table + (long long)b * P.max_blocks + p_lo) : -1;
     const int split = (b == b_begin) ? split_begin : ns0;
     const bool single = (ns1 - ns0) == 1;
     const int n_row = P.causal ? L - P.s_q + 1 + qj : L;  // keys this row sees
@@ -250,7 +266,8 @@ void mla_decode_kernel(DecodeParams P) {
       for (int dt = 0; dt < 16; ++dt) mfma32_agpr_zero(acc[dt], zero8);
       m_ref = m_seen;
       l_run = 0.f;
-      load_page<NW>(P, b, p_lo, L, lds, wave, lane);
+      int pid_next = p_lo + 1 < p_hi ? fetch_pid(P, b, p_lo + 1) : 0;
+      load_page<NW>(P, b, p_lo, L, lds, wave, lane, pid_first);
       bool restart = false;
       for (int p = p_lo, k = 0; p < p_hi; ++p, ++k) {
         wait_vmem_all();
@@ -258,7 +275,8 @@ void mla_decode_kernel(DecodeParams P) {
         if (k > 0 && restart_flags[(k + 2) % 3]) { restart = true; break; }  // slot of page k - 1
         restart_flags[(k + 1) % 3] = 0;
         MLA_LDS char* cur = lds + (k & 1) * kStageBytes;
-        if (p + 1 < p_hi) load_page<NW>(P, b, p + 1, L, lds + ((k + 1) & 1) * kStageBytes, wave, lane);
+        if (p + 1 < p_hi) load_page<NW>(P, b, p + 1, L, lds + ((k + 1) & 1) * kStageBytes, wave, lane, pid_next);
+        if (p + 2 < p_hi) pid_next = fetch_pid(P, b, p + 2);
 
 #pragma unroll 1
         for (int tt = 0; tt < 2; ++tt) {
@@ -346,30 +364,39 @@ void mla_decode_kernel(DecodeParams P) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float lse_v = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
-    if (P.q_lat_lo != nullptr) {
+    const int row0 = rb * (NW * 32);                  // first row of this row block
+    if (single && P.q_lat_lo != nullptr) {
       // The scores used q_lat rounded to bf16; the residue q_lo = q_lat - bf16(q_lat)
       // shifts score t by scale * (q_lo . c_t). lse is smooth in the scores with
       // d lse / d s_t = p_t, so to first order lse moves by
       // scale * sum_t p_t (q_lo . c_t) = scale * (q_lo . o_lat): one 512-long dot
       // per row instead of a second pass over every token. The dropped second
       // order term is at most half the square of the largest shift (~1e-5).
-      const uint2* qlo = reinterpret_cast<const uint2*>(P.q_lat_lo + qrow * kDLat + 4 * g);
-      uint2 qv[64];
-#pragma unroll
-      for (int i = 0; i < 64; ++i) qv[i] = qlo[(i >> 2) * 8 + (i & 3) * 2];  // d = 32 dt + 8 vq + 4 g
+      // Split pieces leave this to mla_combine, which applies it to the merged row.
+      // The wave's 32 q_lo rows go to LDS (both page buffers are idle after the
+      // piece's last barrier), kQloStride apart so the 8-byte reads spread over
+      // the banks; each lane then reads the values that match its accumulators.
+      MLA_LDS char* qs = lds + wave * (32 * kQloStride);
+      const char* src = reinterpret_cast<const char*>(P.q_lat_lo) + lane * 16;
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const long long r = (long long)b * M + min(row0 + wave * 32 + i, M - 1);
+        g2lds16(src + r * (kDLat * 2), qs + i * kQloStride);
+      }
+      wait_vmem_all();
+      const MLA_LDS char* qrow_l = qs + r32 * kQloStride + 8 * g;
       float dot = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq) {
-          const bf16x4 q4 = __builtin_bit_cast(bf16x4, qv[dt * 4 + vq]);
+          const bf16x4 q4 = *reinterpret_cast<const MLA_LDS bf16x4*>(qrow_l + 64 * dt + 16 * vq);  // d = 32 dt + 8 vq + 4 g
 #pragma unroll
           for (int e = 0; e < 4; ++e) dot += acc[dt][4 * vq + e] * (float)q4[e];
         }
       dot += __shfl_xor(dot, 32);
       if (l_tot > 0.f) lse_v += P.scale * dot * inv_l;
     }
-    const int row0 = rb * (NW * 32);                  // first row of this row block
     const int nrows = min(NW * 32, M - row0);         // valid rows in it
     const int lrow = wave * 32 + r32;                 // this lane's row within the block
     if (single) {
@@ -453,6 +480,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  float dot = 0.f;  // q_lo . o_lat for the first-order lse correction (see the decode epilogue)
+  const uint16_t* qlo = P.q_lat_lo != nullptr ? P.q_lat_lo + orow * kDLat : nullptr;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     bf16x4 w;
@@ -461,8 +490,16 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
     w[2] = (__bf16)(o[q][2] * inv);
     w[3] = (__bf16)(o[q][3] * inv);
     *reinterpret_cast<bf16x4*>(out + 128 * q + 4 * t) = w;
+    if (qlo != nullptr) {
+      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(qlo + 128 * q + 4 * t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot += o[q][e] * inv * (float)q4[e];
+    }
   }
-  if (t == 0) P.lse[orow] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);  // the row's 32 threads
+  if (t == 0)
+    P.lse[orow] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 + P.scale * dot : -INFINITY;
 }
 
 // The page loader on its own: one workgroup per (page, sequence).
@@ -475,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) void mla_gather_kernel(DecodeParams P, con
   const int L = P.seqlens[b];
   if (page * kPage >= L) return;
   const int lane = threadIdx.x & 63, wave = wave_id_uniform();
-  load_page<NW>(P, b, page, L, lds, wave, lane);
+  load_page<NW>(P, b, page, L, lds, wave, lane, fetch_pid(P, b, page));
   wait_vmem_all();
   __syncthreads();
   const int rows = min(kPage, L - page * kPage);
