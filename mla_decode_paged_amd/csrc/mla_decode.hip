@@ -53,7 +53,7 @@
 namespace mla {
 
 __device__ int g_device_error = 0;
-__device__ const uint4 g_zero_row[kRowBytes / 16] = {};
+__device__ const uint4 g_zero_page[kPage * kRowBytes / 16] = {};  // stands in for a bad page
 
 // LDS page layout (bytes): block (rb, cb) = rows 8rb..8rb+7, chunks 8cb..8cb+7
 // sits at rb * kBlkRowStride + cb * 1024; inside it, row r's chunk c is at
@@ -61,10 +61,13 @@ __device__ const uint4 g_zero_row[kRowBytes / 16] = {};
 constexpr int kBlkBytes = 1024;                              // one wave load instruction
 constexpr int kBlkCols = kRowBytes / 128;                    // 9 blocks per 8 rows
 constexpr int kBlkRowStride = kBlkCols * kBlkBytes + 32;     // 9248: +32 B rotates banks by 8
-constexpr int kStageBytes = (kPage / 8) * kBlkRowStride;     // 73984 per page buffer
+constexpr int kTile = 32;                                    // tokens per tile (half a page)
+constexpr int kTileStageBytes = (kTile / 8) * kBlkRowStride; // 36992 per tile buffer
+constexpr int kStages = 4;                                   // tile buffers in LDS
+constexpr int kStageBytes = 2 * kTileStageBytes;             // a whole page (the gather kernel)
 constexpr int kRowsBytes8 = 8 * kRowBytes;                   // 9216: 8 cache rows in HBM
 constexpr int kQloStride = kDLat * 2 + 16;                   // q_lo rows staged in LDS: 1040 B apart
-static_assert(4 * 32 * kQloStride <= 2 * kStageBytes, "q_lo staging must fit in the page buffers");
+static_assert(4 * 32 * kQloStride <= kStages * kTileStageBytes, "q_lo staging must fit in the tile buffers");
 
 __device__ __forceinline__ int chunk_swz(int lr) { return ((lr >> 1) & 1) * 4 + (lr >> 2); }
 __device__ __forceinline__ int lds_off(int r, int c) {
@@ -103,55 +106,68 @@ __device__ __forceinline__ int ldc(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
-// Block-table entry of `page` of sequence b (-1 past the table). The kernels
-// read it one page ahead of load_page, so its latency hides behind a page of
-// work instead of stalling the loader.
+// Block-table entry of `page` of sequence b (-1 past the table), through the
+// scalar cache: consecutive pages of a sequence share a cache line.
 __device__ __forceinline__ int fetch_pid(const DecodeParams& P, int b, int page) {
-  return page < P.max_blocks ? P.block_table[(long long)b * P.max_blocks + page] : -1;
+  return page < P.max_blocks ? ldc(P.block_table + (long long)b * P.max_blocks + page) : -1;
 }
 
-// Load one page of sequence b into `stage` with direct-to-LDS loads: wave w
-// copies block rows [w * 8/NW, (w+1) * 8/NW). Lane l always fills in-block
-// position l: row l / 8 and chunk (l % 8) ^ swz(l / 8) of the block, so its
-// HBM address is page + lane_off + (uniform block offset). Page ids outside
-// the cache or past the block table become zero pages and set the device
-// error word; rows past the cache length read the zero row. Every branch is
-// uniform (see the note on divergence at the kernel).
+// Tile loader: one tile (32 tokens, half a page, 4 block rows) of sequence b
+// goes to an LDS tile buffer with direct-to-LDS loads; wave w copies block
+// rows [w * 4/NW, (w+1) * 4/NW) of it, 9 wave instructions per block row.
+// Lane l always fills in-block position l (row l / 8, chunk (l % 8) ^ swz(l / 8)),
+// so its HBM address is a uniform page base plus a per-lane 32-bit offset plus
+// a uniform block offset. setup() resolves the page; issue(i) sends
+// instruction i, so the decode kernel can spread the instructions of a tile
+// between its matrix instructions. Rows past the cache length repeat the
+// page's last cached row (finite data whose scores the kernel masks, so they
+// weigh exactly zero); page ids outside the cache or past the block table
+// read a zero page and set the device error word. Every branch is uniform
+// (see the note on divergence at the kernel).
 template <int NW>
-__device__ __forceinline__ void load_page(const DecodeParams& P, int b, int page, int L, MLA_LDS char* stage,
-                                          int wave, int lane, int pid_fetched) {
-  const bool in_table = page < P.max_blocks;
-  const long long pid = __builtin_amdgcn_readfirstlane(pid_fetched);  // from fetch_pid
-  const bool ok = in_table && pid >= 0 && pid < P.num_pages;
-  if (!ok) flag_error(in_table ? MLA_DEVERR_PAGE_ID : MLA_DEVERR_SEQ_TOO_LONG);
-  const int nvalid = min(kPage, L - page * kPage);
-  const char* page_base = reinterpret_cast<const char*>(P.kv) + (ok ? pid : 0) * (long long)(kPage * kRowBytes);
-  const int lr = lane >> 3, lc = (lane & 7) ^ chunk_swz(lane >> 3);
-  const int lane_off = lr * kRowBytes + lc * 16;
-  constexpr int kRB = 8 / NW;  // block rows per wave
-  if (ok && nvalid == kPage) {
+struct TileLoad {
+  static constexpr int kRows = 4 / NW;               // block rows per wave
+  static constexpr int kInstr = kRows * kBlkCols;    // wave instructions per tile
+  const char* base;
+  unsigned voff[kRows];
+  unsigned dst;  // LDS byte address of the wave's first block row
+
+  __device__ __forceinline__ void setup(const DecodeParams& P, int page, int half, int L, int pid,
+                                        MLA_LDS char* stage, int wave, int lane) {
+    const bool in_table = page < P.max_blocks;
+    const bool ok = in_table && pid >= 0 && pid < P.num_pages;
+    if (!ok) flag_error(in_table ? MLA_DEVERR_PAGE_ID : MLA_DEVERR_SEQ_TOO_LONG);
+    base = ok ? reinterpret_cast<const char*>(P.kv) + (long long)pid * (kPage * kRowBytes)
+              : reinterpret_cast<const char*>(g_zero_page);
+    const int last = ok ? min(kPage, L - page * kPage) - 1 : kPage - 1;  // last row to read
+    const int lr = lane >> 3, lc = (lane & 7) ^ chunk_swz(lane >> 3);
 #pragma unroll
-    for (int i = 0; i < kRB; ++i) {
-      const int rb = wave * kRB + i;
-      const char* src = page_base + rb * kRowsBytes8 + lane_off;
-      MLA_LDS char* dst = stage + rb * kBlkRowStride;
-#pragma unroll
-      for (int cb = 0; cb < kBlkCols; ++cb) g2lds16(src + cb * 128, dst + cb * kBlkBytes);
+    for (int r = 0; r < kRows; ++r) {
+      const int row = half * kTile + (wave * kRows + r) * 8 + lr;  // row within the page
+      voff[r] = (unsigned)(min(row, last) * kRowBytes + lc * 16);
     }
-  } else {  // last page of a sequence, or a bad page id: pick rows by a bit select
-    const uintptr_t zero = reinterpret_cast<uintptr_t>(g_zero_row) + lc * 16;
-#pragma unroll
-    for (int i = 0; i < kRB; ++i) {
-      const int rb = wave * kRB + i;
-      const uintptr_t real = reinterpret_cast<uintptr_t>(page_base + rb * kRowsBytes8 + lane_off);
-      const uintptr_t m = (uintptr_t)0 - (uintptr_t)(ok && rb * 8 + lr < nvalid);
-      const uintptr_t src = zero ^ ((real ^ zero) & m);
-      MLA_LDS char* dst = stage + rb * kBlkRowStride;
-#pragma unroll
-      for (int cb = 0; cb < kBlkCols; ++cb)
-        g2lds16(reinterpret_cast<const void*>(src + (uintptr_t)(cb * 128)), dst + cb * kBlkBytes);
-    }
+    dst = (unsigned)(uintptr_t)(stage + wave * kRows * kBlkRowStride);
   }
+  // Not seen by the compiler's wait insertion: callers wait with vmcnt.
+  __device__ __forceinline__ void issue(int i) const {
+    const int r = i / kBlkCols, cb = i % kBlkCols;
+    g2lds16_untracked(base, voff[r] + cb * 128, dst + r * kBlkRowStride + cb * kBlkBytes);
+  }
+};
+
+// Workgroup barrier of the tile pipeline. The wave's LDS operations finish
+// first; its direct-to-LDS loads of later tiles stay in flight (each wave has
+// already waited for its share of the tile the barrier publishes). A fenced
+// __syncthreads would wait for those loads too.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt for vector memory only (expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Divergence note: the kernel keeps every branch wave-uniform. Register
@@ -163,12 +179,10 @@ __device__ __forceinline__ void load_page(const DecodeParams& P, int b, int page
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(DecodeParams P) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
-  // restart requests, rotating over three slots: page iteration k writes
-  // slot k % 3, every wave reads it after the next barrier, and slot
-  // (k + 1) % 3 is cleared then (all reads of it finished one barrier earlier,
-  // its next writer starts one barrier later), so all waves see one value
-  __shared__ int restart_flags[3];
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kTileStageBytes];
+  // restart request of the current pass: cleared when a pass starts, set by
+  // any wave whose scores outgrow the reference, read by all after the pass
+  __shared__ int restart_flag;
   MLA_LDS char* lds = (MLA_LDS char*)(smem);
 
   const int lane = threadIdx.x & 63;
@@ -198,11 +212,16 @@ void mla_decode_kernel(DecodeParams P) {
 
   const int M = P.M;
   const int row = rb * (NW * 32) + wave * 32 + r32;  // query row within the sequence
-  const bool row_ok = row < M;
-  const int row_c = min(row, M - 1);                 // padding rows alias the last row (never stored)
+  // padding rows alias the last row: they repeat its work (so they raise no
+  // restart of their own) and are never stored
+  const int row_c = min(row, M - 1);
   const int qj = row_c >> P.log2_h;                  // query token index of this row (h is a power of 2)
-  const unsigned keep = row_ok ? 0xffffffffu : 0u;
   const bf16x8 zero8 = bf16x8{};
+  // Tiles in flight: while tile j is multiplied, the loads of tile j + kAhead
+  // go out between its matrix instructions (kAhead + 1 <= kStages buffers).
+  constexpr int kNLd = TileLoad<NW>::kInstr;
+  constexpr int kAhead = NW == 1 ? 2 : 3;  // keeps the outstanding count within vmcnt's 63
+  static_assert((kAhead - 1) * kNLd < 64 && kAhead < kStages, "load pipeline depth");
 
   // LDS-relative constants of this lane (see the layout at kBlkRowStride).
   // K fragment for k-step ks of a 32-token tile: token r32, chunk 2 ks + g
@@ -242,118 +261,136 @@ void mla_decode_kernel(DecodeParams P) {
     const int n_min = P.causal ? L - P.s_q + 1 : L;       // fewest keys of any row
 
     const long long qrow = (long long)b * M + row_c;
+    const int tok0 = p_lo * kPage;
+    const int n_tiles = (min(p_hi * kPage, L) - tok0 + kTile - 1) / kTile;  // tiles holding cached tokens
     bf16x8 qf[36];
     {
       const u32x4* ql = reinterpret_cast<const u32x4*>(P.q_lat + qrow * kDLat) + g;
       const u32x4* qp = reinterpret_cast<const u32x4*>(P.q_pe + qrow * kDRope) + g;
 #pragma unroll
-      for (int ks = 0; ks < 32; ++ks) qf[ks] = as_bf16x8(ql[2 * ks] & keep);
+      for (int ks = 0; ks < 32; ++ks) qf[ks] = as_bf16x8(ql[2 * ks]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = as_bf16x8(qp[2 * ks] & keep);
+      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = as_bf16x8(qp[2 * ks]);
     }
 
     // Softmax reference. Probabilities are exp2(x - m_ref) with m_ref fixed
     // for the whole piece, so the accumulators never need rescaling; m_ref is
     // the row's first finite tile max. If a later score exceeds it by more
     // than kRefSlack (where fp32 sums could start to overflow), the whole
-    // workgroup restarts the piece with the largest max seen so far.
+    // workgroup runs the piece again with the row max of the first pass.
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     f32x16 acc[16];
     for (;;) {  // restart loop: runs once unless a score outgrows m_ref
-      __syncthreads();  // every wave is done with both page buffers and the flags
-      restart_flags[0] = restart_flags[1] = restart_flags[2] = 0;  // every lane writes 0
+      __syncthreads();  // every wave is done with the tile buffers and the flags
+      restart_flag = 0;  // every lane writes 0
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) mfma32_agpr_zero(acc[dt], zero8);
       m_ref = m_seen;
       l_run = 0.f;
-      int pid_next = p_lo + 1 < p_hi ? fetch_pid(P, b, p_lo + 1) : 0;
-      load_page<NW>(P, b, p_lo, L, lds, wave, lane, pid_first);
-      bool restart = false;
-      for (int p = p_lo, k = 0; p < p_hi; ++p, ++k) {
-        wait_vmem_all();
-        __syncthreads();
-        if (k > 0 && restart_flags[(k + 2) % 3]) { restart = true; break; }  // slot of page k - 1
-        restart_flags[(k + 1) % 3] = 0;
-        MLA_LDS char* cur = lds + (k & 1) * kStageBytes;
-        if (p + 1 < p_hi) load_page<NW>(P, b, p + 1, L, lds + ((k + 1) & 1) * kStageBytes, wave, lane, pid_next);
-        if (p + 2 < p_hi) pid_next = fetch_pid(P, b, p + 2);
-
+      TileLoad<NW> ld;
+      int pid = -1;  // page id of the last tile set up
 #pragma unroll 1
-        for (int tt = 0; tt < 2; ++tt) {
-          MLA_LDS char* tile = cur + tt * 4 * kBlkRowStride;
-          // ---- S^T = K Q^T (576 deep), fragments read four k-steps ahead ----
-          // the sched barriers keep the scheduler from hoisting every fragment
-          // read (they would not fit in VGPRs)
-          f32x16 sc = f32x16{};
-          {
-            bf16x8 kr[4];
+      for (int t = 0; t < min(kAhead, n_tiles); ++t) {
+        if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
+        ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kr[i] = lds_read16(tile, a_base[i]);
-#pragma unroll
-            for (int ks = 0; ks < 36; ++ks) {
-              sc = mfma32(kr[ks & 3], qf[ks], sc);
-              if (ks + 4 < 36) kr[ks & 3] = lds_read16(tile, a_base[(ks + 4) & 3] + ((ks + 4) >> 2) * kBlkBytes);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
+        for (int i = 0; i < kNLd; ++i) ld.issue(i);
+      }
+      for (int j = 0; j < n_tiles; ++j) {
+        // this wave's loads of tile j are done once at most the later tiles'
+        // remain; the barrier then covers every wave's share
+        const int later = min(kAhead - 1, n_tiles - 1 - j);
+        if (later >= 2) wait_vmcnt<kAhead >= 3 ? 2 * kNLd : 0>();
+        else if (later == 1) wait_vmcnt<kNLd>();
+        else wait_vmcnt<0>();
+        barrier_keep_loads();
+        const bool more = j + kAhead < n_tiles;
+        if (more) {  // tile j + kAhead reuses the buffer of tile j - 1
+          const int t = j + kAhead;
+          if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
+          ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        MLA_LDS char* tile = lds + (j % kStages) * kTileStageBytes;
+        // load instruction slots: the 68 matrix instructions of a tile carry
+        // the kNLd loads of tile j + kAhead, evenly spaced
+#define MLA_LOAD_SLOT(m)                                                          \
+  if ((((m) + 1) * kNLd) / 68 != ((m) * kNLd) / 68 && more) ld.issue(((m) * kNLd) / 68);
 
-          // ---- softmax numerators, base 2 ----
-          // sc element v is token p*64 + tt*32 + 8*(v/4) + 4*g + v%4
-          const int t0 = p * kPage + tt * 32 + 4 * g;
-          if (p * kPage + tt * 32 + 32 > n_min) {  // some token of this tile is masked for some row
+        // ---- S^T = K Q^T (576 deep), fragments read four k-steps ahead ----
+        // the sched barriers keep the scheduler from hoisting every fragment
+        // read (they would not fit in VGPRs)
+        f32x16 sc = f32x16{};
+        {
+          bf16x8 kr[4];
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (t0 + 8 * (v >> 2) + (v & 3) >= n_row) sc[v] = -INFINITY;
-          }
-          float mx = sc[0];
+          for (int i = 0; i < 4; ++i) kr[i] = lds_read16(tile, a_base[i]);
 #pragma unroll
-          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32)) * P.scale_log2e;  // scale > 0 commutes with max
-          m_seen = fmaxf(m_seen, mx);
-          if (m_ref == -INFINITY) m_ref = mx;  // nothing accumulated yet for this row
-          if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRefSlack) != 0ull) restart_flags[k % 3] = 1;
-          const float msub = m_ref == -INFINITY ? 0.f : m_ref;
-          float psum = 0.f;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            sc[v] = fast_exp2(sc[v] * P.scale_log2e - msub);
-            psum += sc[v];
-          }
-          l_run += psum;
-          const bf16x8 pb0 = pack8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
-          const bf16x8 pb1 = pack8(sc[8], sc[9], sc[10], sc[11], sc[12], sc[13], sc[14], sc[15]);
-
-          // ---- O^T += V^T P^T over this tile's 32 tokens, fragments four steps ahead ----
-          {
-            bf16x4 vr[4][2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {  // step it = dt * 2 + kk
-              const int o = v_base[(i >> 1) & 1] + ((i >> 1) >> 1) * kBlkBytes + 2 * (i & 1) * kBlkRowStride;
-              vr[i][0] = lds_read_tr4(tile, o);
-              vr[i][1] = lds_read_tr4(tile, o + kBlkRowStride);
-            }
-#pragma unroll
-            for (int it = 0; it < 32; ++it) {
-              const int dt = it >> 1, kk = it & 1;
-              mfma32_agpr(acc[dt], cat4(vr[it & 3][0], vr[it & 3][1]), kk ? pb1 : pb0);
-              if (it + 4 < 32) {
-                const int n = it + 4, ndt = n >> 1;
-                const int o = v_base[ndt & 1] + (ndt >> 1) * kBlkBytes + 2 * (n & 1) * kBlkRowStride;
-                vr[it & 3][0] = lds_read_tr4(tile, o);
-                vr[it & 3][1] = lds_read_tr4(tile, o + kBlkRowStride);
-              }
-              __builtin_amdgcn_sched_barrier(0);
-            }
+          for (int ks = 0; ks < 36; ++ks) {
+            sc = mfma32(kr[ks & 3], qf[ks], sc);
+            if (ks + 4 < 36) kr[ks & 3] = lds_read16(tile, a_base[(ks + 4) & 3] + ((ks + 4) >> 2) * kBlkBytes);
+            MLA_LOAD_SLOT(ks)
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
+
+        // ---- softmax numerators, base 2 ----
+        // sc element v is token tok0 + 32 j + 8 (v / 4) + 4 g + v % 4
+        const int t0 = tok0 + j * kTile + 4 * g;
+        if (tok0 + j * kTile + kTile > n_min) {  // some token of this tile is masked for some row
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (t0 + 8 * (v >> 2) + (v & 3) >= n_row) sc[v] = -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * P.scale_log2e;  // scale > 0 commutes with max
+        m_seen = fmaxf(m_seen, mx);
+        if (m_ref == -INFINITY) m_ref = mx;  // nothing accumulated yet for this row
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRefSlack) != 0ull) restart_flag = 1;
+        const float msub = m_ref == -INFINITY ? 0.f : m_ref;
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          sc[v] = fast_exp2(sc[v] * P.scale_log2e - msub);
+          psum += sc[v];
+        }
+        l_run += psum;
+        const bf16x8 pb0 = pack8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
+        const bf16x8 pb1 = pack8(sc[8], sc[9], sc[10], sc[11], sc[12], sc[13], sc[14], sc[15]);
+
+        // ---- O^T += V^T P^T over this tile's 32 tokens, fragments four steps ahead ----
+        {
+          bf16x4 vr[4][2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {  // step it = dt * 2 + kk
+            const int o = v_base[(i >> 1) & 1] + ((i >> 1) >> 1) * kBlkBytes + 2 * (i & 1) * kBlkRowStride;
+            vr[i][0] = lds_read_tr4(tile, o);
+            vr[i][1] = lds_read_tr4(tile, o + kBlkRowStride);
+          }
+#pragma unroll
+          for (int it = 0; it < 32; ++it) {
+            const int dt = it >> 1, kk = it & 1;
+            mfma32_agpr(acc[dt], cat4(vr[it & 3][0], vr[it & 3][1]), kk ? pb1 : pb0);
+            if (it + 4 < 32) {
+              const int n = it + 4, ndt = n >> 1;
+              const int o = v_base[ndt & 1] + (ndt >> 1) * kBlkBytes + 2 * (n & 1) * kBlkRowStride;
+              vr[it & 3][0] = lds_read_tr4(tile, o);
+              vr[it & 3][1] = lds_read_tr4(tile, o + kBlkRowStride);
+            }
+            MLA_LOAD_SLOT(36 + it)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#undef MLA_LOAD_SLOT
       }
-      if (!restart) {
-        wait_vmem_all();
-        __syncthreads();
-        restart = restart_flags[(p_hi - p_lo - 1) % 3] != 0;
-      }
-      if (!restart) break;
-      wait_vmem_all();  // a restart may leave the next page's loads in flight
+      wait_vmem_all();
+      __syncthreads();
+      if (restart_flag == 0) break;
+      // a score outgrew the reference: the pass ran to its end (its sums may
+      // have overflowed) and m_seen is now the row's true max, so the next
+      // pass cannot restart again
     }
     mfma_drain();
 
@@ -399,26 +436,39 @@ void mla_decode_kernel(DecodeParams P) {
     }
     const int nrows = min(NW * 32, M - row0);         // valid rows in it
     const int lrow = wave * 32 + r32;                 // this lane's row within the block
+    // Rows leave through LDS: each lane holds 4-value pieces of one row, so
+    // direct stores would write 32 rows x 32 bytes per instruction. The wave
+    // puts its 32 rows into its own LDS rows (kQloStride apart, so the
+    // writes of 16 rows hit distinct banks), then every store instruction
+    // writes one whole contiguous row piece of 1 KB. Only this wave touches
+    // its LDS rows and one wave's LDS operations complete in order, so no
+    // barrier is needed; the tile buffers are idle after the piece's last
+    // barrier. Buffer resources sized to the valid rows drop the writes of
+    // padding rows.
+    MLA_LDS char* tw = lds + wave * (32 * kQloStride);
+    const int wr = r32 * kQloStride;  // this lane's row in the wave's LDS rows
     if (single) {
       const long long rbase = (long long)b * M + row0;
       const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
           P.o_lat + rbase * kDLat, 0, nrows * kDLat * 2, kBufferWord3);
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(P.lse + rbase, 0, nrows * 4,
                                                                           kBufferWord3);
-      const int off = lrow * kDLat * 2 + 8 * g;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq) {
+        for (int vq = 0; vq < 4; ++vq) {  // d = 32 dt + 8 vq + 4 g + e
           bf16x4 w;
           w[0] = (__bf16)(acc[dt][4 * vq + 0] * inv_l);
           w[1] = (__bf16)(acc[dt][4 * vq + 1] * inv_l);
           w[2] = (__bf16)(acc[dt][4 * vq + 2] * inv_l);
           w[3] = (__bf16)(acc[dt][4 * vq + 3] * inv_l);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), ro, off + (dt * 32 + 8 * vq) * 2,
-                                                0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          *reinterpret_cast<MLA_LDS bf16x4*>(tw + wr + (dt * 32 + 8 * vq + 4 * g) * 2) = w;
         }
+#pragma unroll 8
+      for (int k = 0; k < 32; ++k) {  // row wave * 32 + k: 64 lanes x 16 bytes
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + lane * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 2) + lane * 16, 0, 0);
+      }
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
     } else {
       const long long pbase = (long long)split * M + row0;
@@ -426,19 +476,27 @@ void mla_decode_kernel(DecodeParams P) {
           P.part_o + pbase * kDLat, 0, nrows * kDLat * 4, kBufferWord3);
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(P.part_lse + pbase, 0, nrows * 4,
                                                                           kBufferWord3);
-      const int off = lrow * kDLat * 4 + 16 * g;
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt)
+      for (int hv = 0; hv < 2; ++hv) {  // fp32 rows are 2 KB: two rounds of 256 values
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq) {
-          u32x4 w;
-          w[0] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 0] * inv_l);
-          w[1] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 1] * inv_l);
-          w[2] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 2] * inv_l);
-          w[3] = __builtin_bit_cast(unsigned, acc[dt][4 * vq + 3] * inv_l);
-          __builtin_amdgcn_raw_buffer_store_b128(w, ro, off + (dt * 32 + 8 * vq) * 4, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int dl = 0; dl < 8; ++dl) {
+          const int dt = hv * 8 + dl;
+#pragma unroll
+          for (int vq = 0; vq < 4; ++vq) {
+            f32x4 w;
+            w[0] = acc[dt][4 * vq + 0] * inv_l;
+            w[1] = acc[dt][4 * vq + 1] * inv_l;
+            w[2] = acc[dt][4 * vq + 2] * inv_l;
+            w[3] = acc[dt][4 * vq + 3] * inv_l;
+            *reinterpret_cast<MLA_LDS f32x4*>(tw + wr + (dl * 32 + 8 * vq + 4 * g) * 4) = w;
+          }
         }
+#pragma unroll 8
+        for (int k = 0; k < 32; ++k) {
+          const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + lane * 16);
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 4) + hv * 1024 + lane * 16, 0, 0);
+        }
+      }
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
     }
   }
@@ -512,7 +570,14 @@ __global__ __launch_bounds__(NW * 64) void mla_gather_kernel(DecodeParams P, con
   const int L = P.seqlens[b];
   if (page * kPage >= L) return;
   const int lane = threadIdx.x & 63, wave = wave_id_uniform();
-  load_page<NW>(P, b, page, L, lds, wave, lane, fetch_pid(P, b, page));
+  TileLoad<NW> ld;
+  const int pid = fetch_pid(P, b, page);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    ld.setup(P, page, half, L, pid, lds + half * kTileStageBytes, wave, lane);
+#pragma unroll
+    for (int i = 0; i < TileLoad<NW>::kInstr; ++i) ld.issue(i);
+  }
   wait_vmem_all();
   __syncthreads();
   const int rows = min(kPage, L - page * kPage);

@@ -79,6 +79,16 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, MLA_LDS char* lds_wave
       (MLA_LDS void*)(lds_wave_base), 16, 0, 0);
 }
 
+// The same copy written as inline assembly: `base` (wave-uniform, in SGPRs)
+// plus a per-lane 32-bit offset, landing at LDS byte address lds_addr +
+// 16 * lane. The compiler does not see this load, so it neither counts it in
+// its own wait insertion (where a pending direct-to-LDS load makes it drain
+// every LDS read, lgkmcnt(0), instead of keeping a read-ahead ring) nor waits
+// for it before later LDS accesses: the caller waits (vmcnt) and synchronises.
+__device__ __forceinline__ void g2lds16_untracked(const char* base, unsigned voff, unsigned lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
