@@ -30,8 +30,11 @@ __all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata",
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 PAGE_TOKENS, D_LATENT, D_ROPE, D_ROW, D_NOPE = 64, 512, 64, 576, 128
 META_WORDS = 8
-# fixed cost of one sequence piece in the split plan, in pages
-SPLIT_OVERHEAD = 2
+# Fixed cost of one sequence piece in the split plan, in pages: a piece's
+# query loads, first-tile latency, epilogue stores and share of the merge,
+# measured on MI355X against the per-page cost of the 128-head kernel (a
+# sweep of 0..8 on the 128-head workload is fastest at 6).
+SPLIT_OVERHEAD = 6
 
 _lib = None
 _P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t

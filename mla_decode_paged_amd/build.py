@@ -28,7 +28,11 @@ COMMON = [
 # The decode kernel keeps its 256 output accumulators in AGPRs through inline
 # asm; every other MFMA in that file must then use the VGPR form so that the
 # score tile and the query fragments stay in VGPRs.
-PER_FILE = {"mla_decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+# The decode kernel also keeps every branch wave-uniform (see its divergence
+# note); the atomic optimizer would turn each uniform atomic into a one-lane
+# region, so it is off there.
+PER_FILE = {"mla_decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form",
+                               "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:
