@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run one plain elementwise copy (torch.neg) of MIB MiB so that "
+                         "hardware byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path does not shard "
@@ -151,6 +154,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert mla.take_device_error() == 0
+    if args.copy_calibration > 0:  # reads and writes exactly MIB MiB each
+        src = torch.ones((args.copy_calibration << 18,), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     us = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in ev.items()}
     us_step = wall / args.steps * 1e6
 
