@@ -7,11 +7,14 @@
 // since the decode output is linear in the latent rows, W_UV is applied once
 // to the attention output instead of to every cached token (section 2.2).
 //
-// Each workgroup computes one head's 128-row x 64-column output tile with
-// 32x32x16 bf16 MFMAs. The weight tile W[i][0:K][n0:n0+64] is staged in LDS
-// once; its k runs down LDS rows, so the B operand (8 consecutive k of one
-// column per lane) comes from transposed LDS reads. A rows stream from
-// global memory straight into the A operand (16 contiguous bytes per lane).
+// Each workgroup computes one head's 128-row x NT-column output tile (four
+// waves of 32 rows) with 32x32x16 bf16 MFMAs, as the transposed product
+// C^T = W^T A^T. The weight tile W[i][0:K][n0:n0+NT] is staged in LDS once
+// and read back transposed as the A operand; each lane's B operand (8
+// consecutive k of one row of A) is 16 contiguous bytes of that row, loaded
+// straight from HBM. In the C^T layout a lane holds 4 consecutive output
+// columns of one row per element group, so the tile goes to LDS with 8-byte
+// writes and leaves as whole row segments (NT * 2 contiguous bytes per row).
 #include <hip/hip_runtime.h>
 
 #include "mla_device.h"
@@ -20,60 +23,107 @@
 namespace mla {
 
 constexpr int kGemmRows = 128;  // rows per workgroup: 4 waves x 32
-constexpr int kGemmCols = 64;   // columns per workgroup: 2 MFMA tiles
-constexpr int kGemmLdsStride = kGemmCols * 2 + 16;
+constexpr int kBufferWord3G = 0x00020000;  // raw buffer resource: dword data, bounds-checked
 
-template <int K, int N>
+template <int K, int N, int NT>
 __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                         uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
                                                         int R, int h) {
-  __shared__ __attribute__((aligned(16))) char smem[K * kGemmLdsStride];
+  constexpr int kWPitch = NT * 2 + 16;          // bytes per staged W row (k)
+  constexpr int kOPitch = NT * 2 + 16;          // bytes per staged output row
+  constexpr int kWBytes = K * kWPitch;
+  constexpr int kOBytes = kGemmRows * kOPitch;  // one output plane (hi or lo)
+  constexpr int kSmem = kWBytes > 2 * kOBytes ? kWBytes : 2 * kOBytes;
+  constexpr int kNT = NT / 32;                  // 32-column MFMA tiles per wave
+  constexpr int kKS = K / 16;                   // k-steps
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   MLA_LDS char* lds = (MLA_LDS char*)(smem);
-  const int n0 = blockIdx.x * kGemmCols, r0 = blockIdx.y * kGemmRows, head = blockIdx.z;
+  const int n0 = blockIdx.x * NT, r0 = blockIdx.y * kGemmRows, head = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31, g = lane >> 5, j16 = lane & 15;
 
-  // stage W[head][:, n0 : n0 + 64] (row k of the tile = 128 contiguous bytes)
-  const char* wsrc = reinterpret_cast<const char*>(W + (size_t)head * K * N + n0);
-  constexpr int kChunks = K * kGemmCols / 8;
-  for (int c = threadIdx.x; c < kChunks; c += 256) {
-    const int k = c / (kGemmCols / 8), ch = c % (kGemmCols / 8);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(wsrc + (size_t)k * N * 2 + ch * 16);
-    *(MLA_LDS u32x4*)(lds + k * kGemmLdsStride + ch * 16) = v;
+  // this lane's row of A (padding rows repeat the last row and are never stored)
+  const int row = min(r0 + wave * 32 + r32, R - 1);
+  const u32x4* arow = reinterpret_cast<const u32x4*>(A + ((size_t)row * h + head) * K) + g;
+  bf16x8 af[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) af[ks] = as_bf16x8(arow[2 * ks]);
+
+  // stage W[head][:, n0 : n0 + NT]: K rows of NT * 2 bytes, all loads first
+  {
+    constexpr int kRowChunks = NT / 8;
+    constexpr int kPer = K * kRowChunks / 256;
+    const char* wsrc = reinterpret_cast<const char*>(W + (size_t)head * K * N + n0);
+    u32x4 t[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + 256 * i, k = c / kRowChunks, ch = c % kRowChunks;
+      t[i] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)k * N * 2 + ch * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + 256 * i, k = c / kRowChunks, ch = c % kRowChunks;
+      *(MLA_LDS u32x4*)(lds + k * kWPitch + ch * 16) = t[i];
+    }
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r32 = lane & 31, g = lane >> 5, j16 = lane & 15;
-  const int row = r0 + wave * 32 + r32;
-  const bool ok = row < R;
-  const unsigned keep = ok ? 0xffffffffu : 0u;
-  const u32x4* arow = reinterpret_cast<const u32x4*>(A + ((size_t)(ok ? row : 0) * h + head) * K) + g;
   // transposed-read address: k row 16 ks + 8 g + j16/4, column 16*((lane/16)&1) + 4*(j16&3)
-  const int b_off = (8 * g + (j16 >> 2)) * kGemmLdsStride + (16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
-
-  f32x16 c0 = f32x16{}, c1 = f32x16{};
-#pragma unroll 4
-  for (int ks = 0; ks < K / 16; ++ks) {
-    const bf16x8 a = as_bf16x8(arow[2 * ks] & keep);
-    const int o = b_off + 16 * ks * kGemmLdsStride;
-    const bf16x8 b0 = cat4(lds_read_tr4(lds, o), lds_read_tr4(lds, o + 4 * kGemmLdsStride));
-    const bf16x8 b1 = cat4(lds_read_tr4(lds, o + 64), lds_read_tr4(lds, o + 64 + 4 * kGemmLdsStride));
-    c0 = mfma32(a, b0, c0);
-    c1 = mfma32(a, b1, c1);
-  }
-
-  // lane holds C[row 8*(v/4) + 4*g + v%4][column l%32] of each tile
+  const int w_off = (8 * g + (j16 >> 2)) * kWPitch + (16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
+  f32x16 c[kNT];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int orow = r0 + wave * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-    if (orow < R) {
-      const size_t o = ((size_t)orow * h + head) * N + n0 + r32;
-      const __bf16 h0 = (__bf16)c0[v], h1 = (__bf16)c1[v];
-      out[o] = __builtin_bit_cast(uint16_t, h0);
-      out[o + 32] = __builtin_bit_cast(uint16_t, h1);
-      if (out_lo) {
-        out_lo[o] = bf16_bits(c0[v] - (float)h0);
-        out_lo[o + 32] = bf16_bits(c1[v] - (float)h1);
+  for (int t = 0; t < kNT; ++t) c[t] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const int o = w_off + 16 * ks * kWPitch;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      const bf16x8 wf = cat4(lds_read_tr4(lds, o + 64 * t), lds_read_tr4(lds, o + 64 * t + 4 * kWPitch));
+      c[t] = mfma32(wf, af[ks], c[t]);  // C^T tile t: rows = 32 output columns, columns = 32 rows of A
+    }
+  }
+  __syncthreads();  // every wave is done reading the W tile
+
+  // lane holds C^T[column 32 t + 8 q + 4 g + e][row r32], e = 0..3, in c[t][4 q + e]
+  const int orow = wave * 32 + r32;
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = c[t][4 * q + e];
+        hi[e] = (__bf16)v;
+        lo[e] = (__bf16)(v - (float)hi[e]);
       }
+      const int off = orow * kOPitch + (32 * t + 8 * q + 4 * g) * 2;
+      *reinterpret_cast<MLA_LDS bf16x4*>(lds + off) = hi;
+      if (out_lo != nullptr) *reinterpret_cast<MLA_LDS bf16x4*>(lds + kOBytes + off) = lo;
+    }
+  // each wave stores its own 32 rows (only its own LDS rows are read back)
+  constexpr int kLanesPerRow = NT * 2 / 16;
+  constexpr int kRowsPerInstr = 64 / kLanesPerRow;
+  const int rr = lane / kLanesPerRow, ch = lane % kLanesPerRow;
+  const size_t row_stride = (size_t)h * N * 2;  // bytes between consecutive rows of one head
+  const int valid = min(kGemmRows, R - r0);
+  const unsigned nbytes = (unsigned)((size_t)(valid - 1) * row_stride + NT * 2);
+  uint16_t* obase = out + ((size_t)r0 * h + head) * N + n0;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, nbytes, kBufferWord3G);
+#pragma unroll
+  for (int k = 0; k < 32; k += kRowsPerInstr) {
+    const int lr = wave * 32 + k + rr;
+    const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(lds + lr * kOPitch + ch * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (unsigned)(lr * row_stride) + ch * 16, 0, 0);
+  }
+  if (out_lo != nullptr) {
+    const __amdgpu_buffer_rsrc_t rlo = __builtin_amdgcn_make_buffer_rsrc(
+        out_lo + ((size_t)r0 * h + head) * N + n0, 0, nbytes, kBufferWord3G);
+#pragma unroll
+    for (int k = 0; k < 32; k += kRowsPerInstr) {
+      const int lr = wave * 32 + k + rr;
+      const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(lds + kOBytes + lr * kOPitch + ch * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rlo, (unsigned)(lr * row_stride) + ch * 16, 0, 0);
     }
   }
 }
@@ -99,8 +149,8 @@ extern "C" int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16
     return set_error(MLA_ERR_INVALID_ARG, "%s: q_lat_lo must be 16-byte aligned", fn);
   if (int rc = check_shape(fn, b, s_q, h)) return rc;
   const int R = b * s_q;
-  dim3 grid(kDLat / kGemmCols, (R + kGemmRows - 1) / kGemmRows, h);
-  hipLaunchKernelGGL((head_gemm_kernel<kDNope, kDLat>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+  dim3 grid(kDLat / 128, (R + kGemmRows - 1) / kGemmRows, h);
+  hipLaunchKernelGGL((head_gemm_kernel<kDNope, kDLat, 128>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
                      q_nope, w_uk, q_lat, q_lat_lo, R, h);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -115,8 +165,8 @@ extern "C" int mla_up_v(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o
   if (int rc = check_ptr16(fn, o, "o")) return rc;
   if (int rc = check_shape(fn, b, s_q, h)) return rc;
   const int R = b * s_q;
-  dim3 grid(kDNope / kGemmCols, (R + kGemmRows - 1) / kGemmRows, h);
-  hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+  dim3 grid(kDNope / 64, (R + kGemmRows - 1) / kGemmRows, h);
+  hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 64>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
                      o_lat, w_uv, o, static_cast<uint16_t*>(nullptr), R, h);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
