@@ -80,8 +80,9 @@ const char* mla_last_error(void);
 int mla_num_slots(int b, int s_q, int h, int* num_slots /* host out */);
 
 /* Bytes of workspace mla_decode_paged needs for this shape and slot count:
- * fp32 partial outputs [b + num_slots, M, 512] and lse [b + num_slots, M].
- * Returns 0 on bad arguments. Host query. */
+ * partial rows of split sequences as fp16 [b + num_slots, M, 512] (each row
+ * divided by its largest magnitude), their lse and row scales, fp32
+ * [b + num_slots, M] each. Returns 0 on bad arguments. Host query. */
 size_t mla_workspace_bytes(int b, int s_q, int h, int num_slots);
 
 /* mla_get_metadata - split-KV work plan (FlashMLA usage: planned once per

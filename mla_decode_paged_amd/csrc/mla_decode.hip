@@ -88,8 +88,9 @@ struct DecodeParams {
   const int32_t* seqlens;
   const int32_t* tile_meta;
   const int32_t* num_splits;
-  float* part_o;
+  uint16_t* part_o;   // fp16 bits: partial rows divided by their row scale
   float* part_lse;
+  float* part_scale;  // per partial row: largest |value| of the normalised row
   uint16_t* o_lat;
   float* lse;
   long long num_pages;
@@ -471,38 +472,48 @@ void mla_decode_kernel(DecodeParams P) {
       }
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
     } else {
+      // Split pieces publish fp16 rows scaled by their largest magnitude
+      // (values in [-1, 1], 11 significant bits: half the bytes of fp32 for
+      // the same merged result within rounding) plus the scale and lse.
       const long long pbase = (long long)split * M + row0;
       const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-          P.part_o + pbase * kDLat, 0, nrows * kDLat * 4, kBufferWord3);
+          P.part_o + pbase * kDLat, 0, nrows * kDLat * 2, kBufferWord3);
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(P.part_lse + pbase, 0, nrows * 4,
                                                                           kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(P.part_scale + pbase, 0, nrows * 4,
+                                                                          kBufferWord3);
+      float amax = 0.f;  // row max of |O| (the lane pair l, l + 32 holds one row)
 #pragma unroll
-      for (int hv = 0; hv < 2; ++hv) {  // fp32 rows are 2 KB: two rounds of 256 values
+      for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
-        for (int dl = 0; dl < 8; ++dl) {
-          const int dt = hv * 8 + dl;
+        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(acc[dt][v]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float mul = amax > 0.f ? 1.f / amax : 0.f;
+      const float row_scale = amax * inv_l;
 #pragma unroll
-          for (int vq = 0; vq < 4; ++vq) {
-            f32x4 w;
-            w[0] = acc[dt][4 * vq + 0] * inv_l;
-            w[1] = acc[dt][4 * vq + 1] * inv_l;
-            w[2] = acc[dt][4 * vq + 2] * inv_l;
-            w[3] = acc[dt][4 * vq + 3] * inv_l;
-            *reinterpret_cast<MLA_LDS f32x4*>(tw + wr + (dl * 32 + 8 * vq + 4 * g) * 4) = w;
-          }
+      for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {  // d = 32 dt + 8 vq + 4 g + e
+          _Float16 w0 = (_Float16)(acc[dt][4 * vq + 0] * mul), w1 = (_Float16)(acc[dt][4 * vq + 1] * mul);
+          _Float16 w2 = (_Float16)(acc[dt][4 * vq + 2] * mul), w3 = (_Float16)(acc[dt][4 * vq + 3] * mul);
+          u32x2 w;
+          w[0] = (unsigned)__builtin_bit_cast(unsigned short, w0) | ((unsigned)__builtin_bit_cast(unsigned short, w1) << 16);
+          w[1] = (unsigned)__builtin_bit_cast(unsigned short, w2) | ((unsigned)__builtin_bit_cast(unsigned short, w3) << 16);
+          *reinterpret_cast<MLA_LDS u32x2*>(tw + wr + (dt * 32 + 8 * vq + 4 * g) * 2) = w;
         }
 #pragma unroll 8
-        for (int k = 0; k < 32; ++k) {
-          const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + lane * 16);
-          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 4) + hv * 1024 + lane * 16, 0, 0);
-        }
+      for (int k = 0; k < 32; ++k) {  // row wave * 32 + k: 64 lanes x 16 bytes
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + lane * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 2) + lane * 16, 0, 0);
       }
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, row_scale), rs, lrow * 4, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
     }
   }
 }
 
-// Merge split partials: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k.
+// Merge split partials: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k,
+// with o_k = scale_k * (fp16 row k).
 // One workgroup per (sequence, 8 rows); 32 threads per row, 16 values each.
 __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
   const int b = blockIdx.x;
@@ -522,20 +533,43 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
     if (t == 0) P.lse[orow] = -INFINITY;
     return;
   }
-  float mx = -INFINITY;
-  for (int k = 0; k < n; ++k) mx = fmaxf(mx, P.part_lse[(long long)(ns0 + k) * P.M + row]);
+  // Streaming merge over the pieces, four at a time with every load of a
+  // group issued before any is used: running max m, weights exp(lse_k - m).
+  float mx = -INFINITY, wsum = 0.f;
   f32x4 o[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-  float wsum = 0.f;
-  if (mx != -INFINITY) {
-    for (int k = 0; k < n; ++k) {
-      const long long prow = (long long)(ns0 + k) * P.M + row;
-      const float lk = P.part_lse[prow];
-      const float w = fast_exp2((lk - mx) * 1.4426950408889634f);
-      wsum += w;
-      const f32x4* src = reinterpret_cast<const f32x4*>(P.part_o + prow * kDLat) + t;
+  for (int k0 = 0; k0 < n; k0 += 4) {
+    float lk[4], sk[4];
+    u32x2 src[4][4];  // 4 fp16 values each
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] += w * src[32 * q];
+    for (int i = 0; i < 4; ++i) {
+      const long long prow = (long long)(ns0 + min(k0 + i, n - 1)) * P.M + row;  // short groups repeat the last piece
+      lk[i] = k0 + i < n ? P.part_lse[prow] : -INFINITY;
+      sk[i] = P.part_scale[prow];
+      const u32x2* sp = reinterpret_cast<const u32x2*>(P.part_o + prow * kDLat) + t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) src[i][q] = sp[32 * q];
     }
+    const float m_new = fmaxf(fmaxf(mx, fmaxf(lk[0], lk[1])), fmaxf(lk[2], lk[3]));
+    if (m_new == -INFINITY) continue;  // nothing visible yet (uniform over the row's threads)
+    const float alpha = fast_exp2((mx - m_new) * 1.4426950408889634f);  // 0 when mx = -inf
+    wsum *= alpha;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float w = fast_exp2((lk[i] - m_new) * 1.4426950408889634f);  // 0 for padding entries
+      wsum += w;
+      const float ws = w * sk[i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const unsigned lo16 = src[i][q][0], hi16 = src[i][q][1];
+        o[q][0] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(lo16 & 0xffffu));
+        o[q][1] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(lo16 >> 16));
+        o[q][2] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(hi16 & 0xffffu));
+        o[q][3] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(hi16 >> 16));
+      }
+    }
+    mx = m_new;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float dot = 0.f;  // q_lo . o_lat for the first-order lse correction (see the decode epilogue)
@@ -608,13 +642,16 @@ extern "C" int mla_num_slots(int b, int s_q, int h, int* num_slots) {
   return clear_error();
 }
 
+// Workspace: fp16 partial rows [splits, M, 512], then fp32 lse [splits, M]
+// and fp32 row scales [splits, M], each region 256-byte aligned
+// (splits = b + num_slots bounds the plan's pieces).
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
 extern "C" size_t mla_workspace_bytes(int b, int s_q, int h, int num_slots) {
   if (b < 1 || s_q < 1 || h < 1 || num_slots < 1) return 0;
   const size_t M = (size_t)s_q * h;
   const size_t splits = (size_t)b + num_slots;
-  const size_t o_bytes = splits * M * kDLat * sizeof(float);
-  const size_t lse_bytes = splits * M * sizeof(float);
-  return ((o_bytes + 255) / 256) * 256 + ((lse_bytes + 255) / 256) * 256;
+  return round256(splits * M * kDLat * 2) + 2 * round256(splits * M * sizeof(float));
 }
 
 extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
@@ -657,8 +694,9 @@ extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo,
   P.seqlens = cache_seqlens;
   P.tile_meta = tile_meta;
   P.num_splits = num_splits;
-  P.part_o = reinterpret_cast<float*>(ws);
-  P.part_lse = reinterpret_cast<float*>(ws + ((splits * M_ * kDLat * 4 + 255) / 256) * 256);
+  P.part_o = reinterpret_cast<uint16_t*>(ws);
+  P.part_lse = reinterpret_cast<float*>(ws + round256(splits * M_ * kDLat * 2));
+  P.part_scale = reinterpret_cast<float*>(ws + round256(splits * M_ * kDLat * 2) + round256(splits * M_ * 4));
   P.o_lat = o_lat;
   P.lse = lse;
   P.num_pages = num_pages;

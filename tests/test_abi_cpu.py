@@ -46,13 +46,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_workspace_formula(lib):
-    # fp32 partials [b + slots, M, 512] and lse [b + slots, M], each padded to 256 bytes
-    b, s_q, h, slots = 128, 1, 128, 256
-    M = s_q * h
-    o = (b + slots) * M * 512 * 4
-    l = (b + slots) * M * 4
+    # fp16 partial rows [b + slots, M, 512], fp32 lse and fp32 row scales [b + slots, M],
+    # each region padded to 256 bytes
     pad = lambda x: (x + 255) // 256 * 256
-    assert lib.mla_workspace_bytes(b, s_q, h, slots) == pad(o) + pad(l)
+    for b, s_q, h, slots in [(128, 1, 128, 256), (3, 4, 128, 7), (5, 1, 16, 9)]:
+        M = s_q * h
+        assert lib.mla_workspace_bytes(b, s_q, h, slots) == pad((b + slots) * M * 512 * 2) + 2 * pad((b + slots) * M * 4)
     assert lib.mla_workspace_bytes(0, 1, 128, 8) == 0
 
 
