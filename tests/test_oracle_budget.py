@@ -69,3 +69,51 @@ def test_tiny_config_budget():
     for seed in range(3):
         _, corr = lse_errors(make_inputs("tiny", seed=seed))
         assert corr < 2e-5
+
+
+def _merged_o_lat(inp, pieces: int, partial: str):
+    """o_lat the way the split path computes it: bf16 q_lat scores, bf16 probabilities into
+    PV, each piece normalised and stored as `partial`, merged by lse weights, bf16 out."""
+    kv = f32(inp.kv_cache).astype(np.float64)
+    qp = f32(inp.q_pe).astype(np.float64)
+    q_lat = O.absorb_q(f32(inp.q_nope), f32(inp.w_uk))
+    hi = _bf16(q_lat)
+    out, ref = [], []
+    for b in range(inp.b):
+        L = int(inp.seqlens[b])
+        rows = O.token_rows(kv, inp.block_table, b, L)
+        c, kpe = rows[:, :512], rows[:, 512:]
+        s = (c @ hi[b, 0].T + kpe @ qp[b, 0].T) * inp.scale
+        x = (c @ q_lat[b, 0].T + kpe @ qp[b, 0].T) * inp.scale
+        p = np.exp(x - x.max(0))
+        ref.append((p / p.sum(0)).T @ c)
+        parts = []
+        cuts = np.linspace(0, L, pieces + 1).astype(int)
+        for a, e in zip(cuts[:-1], cuts[1:]):
+            ss = s[a:e].astype(np.float32).astype(np.float64)
+            m = ss.max(0)
+            pe = np.exp(ss - m)
+            l = pe.sum(0)
+            o = (_bf16(pe).T @ c[a:e]) / l[:, None]
+            if partial == "fp32":
+                o = o.astype(np.float32).astype(np.float64)
+            else:  # fp16 rows divided by their largest magnitude, scale kept in fp32
+                sc = np.abs(o).max(1, keepdims=True).astype(np.float32).astype(np.float64)
+                sc[sc == 0] = 1.0
+                o = (o / sc).astype(np.float16).astype(np.float64) * sc
+            parts.append((o, m + np.log(l)))
+        top = max(pp[1].max() for pp in parts)
+        lse = np.log(sum(np.exp(pp[1] - top) for pp in parts)) + top
+        out.append(_bf16(sum(np.exp(pp[1] - lse)[:, None] * pp[0] for pp in parts)))
+    out, ref = np.stack(out), np.stack(ref)
+    return float(np.abs(out - ref).max()), float(np.abs(out - ref).sum() / np.abs(ref).sum())
+
+
+def test_scaled_fp16_partials_match_fp32_partials():
+    """Split pieces hand their rows to the merge as fp16 scaled by the row's largest
+    magnitude: the merged o_lat is as close to the exact result as with fp32 partials."""
+    inp = make_inputs("full_heads", seed=3, seqlens=[300, 1100, 2500])
+    mx32, l1_32 = _merged_o_lat(inp, 3, "fp32")
+    mx16, l1_16 = _merged_o_lat(inp, 3, "fp16s")
+    assert l1_16 < 5e-3 and mx16 < 2e-2
+    assert l1_16 < l1_32 * 1.02 and mx16 < mx32 * 1.1
