@@ -266,12 +266,24 @@ void mla_decode_kernel(DecodeParams P) {
     const int n_tiles = (min(p_hi * kPage, L) - tok0 + kTile - 1) / kTile;  // tiles holding cached tokens
     bf16x8 qf[36];
     {
-      const u32x4* ql = reinterpret_cast<const u32x4*>(P.q_lat + qrow * kDLat) + g;
-      const u32x4* qp = reinterpret_cast<const u32x4*>(P.q_pe + qrow * kDRope) + g;
+      // Buffer loads: a uniform base per sequence plus a 32-bit lane offset
+      // that is rebuilt here (the empty asm hides that it is loop invariant).
+      // A hoisted 64-bit per-lane pointer would be spilled, and reloading it
+      // between the loads made the wave wait for all of them first.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int qr = min(rb * (NW * 32) + wave * 32 + (ln & 31), M - 1);
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(P.q_lat + (long long)b * M * kDLat), 0, M * kDLat * 2, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(P.q_pe + (long long)b * M * kDRope), 0, M * kDRope * 2, kBufferWord3);
+      const int oq = qr * (kDLat * 2) + 16 * (ln >> 5), op = qr * (kDRope * 2) + 16 * (ln >> 5);
 #pragma unroll
-      for (int ks = 0; ks < 32; ++ks) qf[ks] = as_bf16x8(ql[2 * ks]);
+      for (int ks = 0; ks < 32; ++ks)
+        qf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rq, oq + 32 * ks, 0, 0));
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = as_bf16x8(qp[2 * ks]);
+      for (int ks = 0; ks < 4; ++ks)
+        qf[32 + ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rp, op + 32 * ks, 0, 0));
     }
 
     // Softmax reference. Probabilities are exp2(x - m_ref) with m_ref fixed
