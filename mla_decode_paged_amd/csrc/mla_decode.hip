@@ -249,6 +249,14 @@ void mla_decode_kernel(DecodeParams P) {
   }
 
   for (int b = b_begin; b <= b_end; ++b) {
+    // Per-lane values used by a piece are rebuilt from the lane id here (the
+    // empty asm hides that it is loop invariant): kept across pieces they
+    // were spilled, and a reload waits for every outstanding load.
+    int pl = lane;
+    asm volatile("" : "+v"(pl));
+    const int pr32 = pl & 31, pg = pl >> 5;
+    const int prow_c = min(rb * (NW * 32) + wave * 32 + pr32, M - 1);
+    const int pqj = prow_c >> P.log2_h;
     const int L = ldc(P.seqlens + b);
     const int npages = L > 0 ? (L + kPage - 1) / kPage : 0;
     const int p_lo = (b == b_begin) ? page_begin : 0;
@@ -258,10 +266,9 @@ void mla_decode_kernel(DecodeParams P) {
     const int pid_first = p_lo < P.max_blocks ? ldc(P.block_table + (long long)b * P.max_blocks + p_lo) : -1;
     const int split = (b == b_begin) ? split_begin : ns0;
     const bool single = (ns1 - ns0) == 1;
-    const int n_row = P.causal ? L - P.s_q + 1 + qj : L;  // keys this row sees
+    const int n_row = P.causal ? L - P.s_q + 1 + pqj : L;  // keys this row sees
     const int n_min = P.causal ? L - P.s_q + 1 : L;       // fewest keys of any row
 
-    const long long qrow = (long long)b * M + row_c;
     const int tok0 = p_lo * kPage;
     const int n_tiles = (min(p_hi * kPage, L) - tok0 + kTile - 1) / kTile;  // tiles holding cached tokens
     bf16x8 qf[36];
@@ -270,14 +277,12 @@ void mla_decode_kernel(DecodeParams P) {
       // that is rebuilt here (the empty asm hides that it is loop invariant).
       // A hoisted 64-bit per-lane pointer would be spilled, and reloading it
       // between the loads made the wave wait for all of them first.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int qr = min(rb * (NW * 32) + wave * 32 + (ln & 31), M - 1);
+      const int qr = prow_c;
       const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(P.q_lat + (long long)b * M * kDLat), 0, M * kDLat * 2, kBufferWord3);
       const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(P.q_pe + (long long)b * M * kDRope), 0, M * kDRope * 2, kBufferWord3);
-      const int oq = qr * (kDLat * 2) + 16 * (ln >> 5), op = qr * (kDRope * 2) + 16 * (ln >> 5);
+      const int oq = qr * (kDLat * 2) + 16 * pg, op = qr * (kDRope * 2) + 16 * pg;
 #pragma unroll
       for (int ks = 0; ks < 32; ++ks)
         qf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rq, oq + 32 * ks, 0, 0));
@@ -293,22 +298,27 @@ void mla_decode_kernel(DecodeParams P) {
     // workgroup runs the piece again with the row max of the first pass.
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     f32x16 acc[16];
+    TileLoad<NW> ld;
+    int pid = -1;  // page id of the last tile set up
+    // The first tiles go out right behind the query loads, so both arrive
+    // in one memory round trip.
+    auto issue_first_tiles = [&]() {
+#pragma unroll 1
+      for (int t = 0; t < min(kAhead, n_tiles); ++t) {
+        if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
+        ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, pl);
+#pragma unroll
+        for (int i = 0; i < kNLd; ++i) ld.issue(i);
+      }
+    };
+    __syncthreads();   // every wave is done with the LDS use of the previous piece
+    restart_flag = 0;  // every lane writes 0
+    issue_first_tiles();
     for (;;) {  // restart loop: runs once unless a score outgrows m_ref
-      __syncthreads();  // every wave is done with the tile buffers and the flags
-      restart_flag = 0;  // every lane writes 0
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) mfma32_agpr_zero(acc[dt], zero8);
       m_ref = m_seen;
       l_run = 0.f;
-      TileLoad<NW> ld;
-      int pid = -1;  // page id of the last tile set up
-#pragma unroll 1
-      for (int t = 0; t < min(kAhead, n_tiles); ++t) {
-        if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
-        ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
-#pragma unroll
-        for (int i = 0; i < kNLd; ++i) ld.issue(i);
-      }
       for (int j = 0; j < n_tiles; ++j) {
         // this wave's loads of tile j are done once at most the later tiles'
         // remain; the barrier then covers every wave's share
@@ -321,7 +331,7 @@ void mla_decode_kernel(DecodeParams P) {
         if (more) {  // tile j + kAhead reuses the buffer of tile j - 1
           const int t = j + kAhead;
           if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
-          ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
+          ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, pl);
         }
         __builtin_amdgcn_sched_barrier(0);
         MLA_LDS char* tile = lds + (j % kStages) * kTileStageBytes;
@@ -349,7 +359,7 @@ void mla_decode_kernel(DecodeParams P) {
 
         // ---- softmax numerators, base 2 ----
         // sc element v is token tok0 + 32 j + 8 (v / 4) + 4 g + v % 4
-        const int t0 = tok0 + j * kTile + 4 * g;
+        const int t0 = tok0 + j * kTile + 4 * pg;
         if (tok0 + j * kTile + kTile > n_min) {  // some token of this tile is masked for some row
 #pragma unroll
           for (int v = 0; v < 16; ++v)
@@ -404,6 +414,9 @@ void mla_decode_kernel(DecodeParams P) {
       // a score outgrew the reference: the pass ran to its end (its sums may
       // have overflowed) and m_seen is now the row's true max, so the next
       // pass cannot restart again
+      __syncthreads();  // every wave has read the flag
+      restart_flag = 0;
+      issue_first_tiles();
     }
     mfma_drain();
 
@@ -427,14 +440,14 @@ void mla_decode_kernel(DecodeParams P) {
       // piece's last barrier), kQloStride apart so the 8-byte reads spread over
       // the banks; each lane then reads the values that match its accumulators.
       MLA_LDS char* qs = lds + wave * (32 * kQloStride);
-      const char* src = reinterpret_cast<const char*>(P.q_lat_lo) + lane * 16;
+      const char* src = reinterpret_cast<const char*>(P.q_lat_lo) + pl * 16;
 #pragma unroll 4
       for (int i = 0; i < 32; ++i) {
         const long long r = (long long)b * M + min(row0 + wave * 32 + i, M - 1);
         g2lds16(src + r * (kDLat * 2), qs + i * kQloStride);
       }
       wait_vmem_all();
-      const MLA_LDS char* qrow_l = qs + r32 * kQloStride + 8 * g;
+      const MLA_LDS char* qrow_l = qs + pr32 * kQloStride + 8 * pg;
       float dot = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt)
@@ -448,7 +461,7 @@ void mla_decode_kernel(DecodeParams P) {
       if (l_tot > 0.f) lse_v += P.scale * dot * inv_l;
     }
     const int nrows = min(NW * 32, M - row0);         // valid rows in it
-    const int lrow = wave * 32 + r32;                 // this lane's row within the block
+    const int lrow = wave * 32 + pr32;                // this lane's row within the block
     // Rows leave through LDS: each lane holds 4-value pieces of one row, so
     // direct stores would write 32 rows x 32 bytes per instruction. The wave
     // puts its 32 rows into its own LDS rows (kQloStride apart, so the
@@ -459,7 +472,7 @@ void mla_decode_kernel(DecodeParams P) {
     // barrier. Buffer resources sized to the valid rows drop the writes of
     // padding rows.
     MLA_LDS char* tw = lds + wave * (32 * kQloStride);
-    const int wr = r32 * kQloStride;  // this lane's row in the wave's LDS rows
+    const int wr = pr32 * kQloStride;  // this lane's row in the wave's LDS rows
     if (single) {
       const long long rbase = (long long)b * M + row0;
       const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
@@ -475,12 +488,12 @@ void mla_decode_kernel(DecodeParams P) {
           w[1] = (__bf16)(acc[dt][4 * vq + 1] * inv_l);
           w[2] = (__bf16)(acc[dt][4 * vq + 2] * inv_l);
           w[3] = (__bf16)(acc[dt][4 * vq + 3] * inv_l);
-          *reinterpret_cast<MLA_LDS bf16x4*>(tw + wr + (dt * 32 + 8 * vq + 4 * g) * 2) = w;
+          *reinterpret_cast<MLA_LDS bf16x4*>(tw + wr + (dt * 32 + 8 * vq + 4 * pg) * 2) = w;
         }
 #pragma unroll 8
       for (int k = 0; k < 32; ++k) {  // row wave * 32 + k: 64 lanes x 16 bytes
-        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + lane * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 2) + lane * 16, 0, 0);
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + pl * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 2) + pl * 16, 0, 0);
       }
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
     } else {
@@ -511,12 +524,12 @@ void mla_decode_kernel(DecodeParams P) {
           u32x2 w;
           w[0] = (unsigned)__builtin_bit_cast(unsigned short, w0) | ((unsigned)__builtin_bit_cast(unsigned short, w1) << 16);
           w[1] = (unsigned)__builtin_bit_cast(unsigned short, w2) | ((unsigned)__builtin_bit_cast(unsigned short, w3) << 16);
-          *reinterpret_cast<MLA_LDS u32x2*>(tw + wr + (dt * 32 + 8 * vq + 4 * g) * 2) = w;
+          *reinterpret_cast<MLA_LDS u32x2*>(tw + wr + (dt * 32 + 8 * vq + 4 * pg) * 2) = w;
         }
 #pragma unroll 8
       for (int k = 0; k < 32; ++k) {  // row wave * 32 + k: 64 lanes x 16 bytes
-        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + lane * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 2) + lane * 16, 0, 0);
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + k * kQloStride + pl * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (wave * 32 + k) * (kDLat * 2) + pl * 16, 0, 0);
       }
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, row_scale), rs, lrow * 4, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, lrow * 4, 0, 0);
