@@ -44,6 +44,29 @@ def algorithmic_work(inp):
     return dict(kv_bytes=kv_bytes, bytes=kv_bytes + q_bytes + out_bytes + int_bytes, flops=flops)
 
 
+TRAFFIC_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_metadata.hip")
+
+
+def recorded_traffic(config: str):
+    """HBM bytes per decode call from the calibrated FETCH_SIZE/WRITE_SIZE runs recorded under
+    profiles/, or None when there is no record for this workload or the kernel sources changed since."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "mla_decode_paged_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    path = os.path.join(ROOT, "profiles", f"mla_decode_{config}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        m = re.search(r"^traffic-record: workload=(\S+) bytes_per_call=(\d+) sources_sha256=([0-9a-f]{64})$",
+                      f.read(), re.M)
+    if not m or m.group(1) != config or m.group(3) != h.hexdigest():
+        return None
+    return int(m.group(2))
+
+
 def cpu_baseline(inp, budget_s: float):
     """Time the CPU oracle as it stands on a bounded sample and scale to one call."""
     import numpy as np
@@ -183,7 +206,8 @@ def main():
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.config),
+                     "traffic_unit": "HBM bytes per call (calibrated counters)",
                      "kernel": "mla_decode_paged call (split kernel + combine)",
                      "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"]},
     }
