@@ -25,6 +25,7 @@ import torch
 
 __all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "decode_paged",
            "up_v", "gather_pages", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
+           "SPLIT_OVERHEAD_FEW_ROWS", "default_split_overhead",
            "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -32,9 +33,14 @@ PAGE_TOKENS, D_LATENT, D_ROPE, D_ROW, D_NOPE = 64, 512, 64, 576, 128
 META_WORDS = 8
 # Fixed cost of one sequence piece in the split plan, in pages: a piece's
 # query loads, first-tile latency, epilogue stores and share of the merge,
-# measured on MI355X against the per-page cost of the 128-head kernel (a
-# sweep of 0..8 on the 128-head workload is fastest at 6).
+# measured on MI355X against the per-page cost of the kernel that runs it.
+# Row blocks of 128 rows (a sweep of 0..8 on the 128-head workload is
+# fastest at 5-6):
 SPLIT_OVERHEAD = 6
+# At most 32 rows (the token-split kernel, whose pages cost about half as
+# much and whose pieces start in a shared burst of first-tile loads; a sweep
+# of 0..16 on the 32-head workload spans 30.1-33.1 us, 30.7 at 2):
+SPLIT_OVERHEAD_FEW_ROWS = 2
 
 _lib = None
 _P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -116,10 +122,16 @@ def workspace_bytes(b: int, s_q: int, h: int, slots: int) -> int:
     return n
 
 
+def default_split_overhead(s_q: int, h: int) -> int:
+    return SPLIT_OVERHEAD_FEW_ROWS if s_q * h <= 32 else SPLIT_OVERHEAD
+
+
 def get_metadata(cache_seqlens: torch.Tensor, slots: int | None = None, s_q: int = 1, h: int = 128,
-                 split_overhead: int = SPLIT_OVERHEAD):
+                 split_overhead: int | None = None):
     """Split-KV plan: (tile_meta int32 [slots, 8], num_splits int32 [b + 1])."""
     b = cache_seqlens.numel()
+    if split_overhead is None:
+        split_overhead = default_split_overhead(s_q, h)
     if slots is None:
         slots = num_slots(b, s_q, h)
     dev = cache_seqlens.device

@@ -537,6 +537,332 @@ void mla_decode_kernel(DecodeParams P) {
   }
 }
 
+// Token-split decode for one block of at most 32 query rows (M <= 32: one
+// tensor-parallel share of the heads, or few heads). One row block gives one
+// wave nothing to share a tile with, so here the four waves of the workgroup
+// split every 32-token tile instead: wave (th, rh) = (wave % 2, wave / 2)
+// scores tokens 16 th .. 16 th + 15 of the tile against rows 16 rh .. 16 rh + 15
+// (16x16x32 MFMAs, K from the same LDS tile image, Q in registers), writes its
+// probabilities to a small LDS buffer, and after a barrier every wave
+// accumulates its own 128 columns of o_lat for all 32 rows from the whole
+// tile (O^T = V^T P^T as in mla_decode_kernel). The loader, the tile
+// pipeline, the fixed softmax reference with restart and the epilogue
+// formats are those of mla_decode_kernel; the reference of a row is shared by
+// the two waves that score it (exchanged once per piece through LDS).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_tsplit_kernel(DecodeParams P) {
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kTileStageBytes];
+  __shared__ __attribute__((aligned(16))) char pbuf[2 * 32 * 32];  // P^T: [k-step][row][16 tokens] bf16 (permuted)
+  __shared__ float xmax[4][16];  // per-wave row maxima (reference and restart exchanges)
+  __shared__ float xl[4][16];    // per-wave row sums
+  __shared__ float xm[2][16];    // the reference of each row
+  __shared__ float xred[4][32];  // per-wave partial row dots / maxima in the epilogue
+  __shared__ int restart_flag;
+  MLA_LDS char* lds = (MLA_LDS char*)(smem);
+  MLA_LDS char* pb = (MLA_LDS char*)(pbuf);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id_uniform();
+  const int th = wave & 1, rh = wave >> 1;
+  const int slot = blockIdx.x;
+  if (slot >= P.num_slots) return;
+  const int* meta = P.tile_meta + slot * MLA_META_WORDS;
+  const int b_begin = ldc(meta + 0), page_begin = ldc(meta + 1), b_end = ldc(meta + 2), page_end = ldc(meta + 3);
+  const int split_begin = ldc(meta + 4);
+  if (b_end < b_begin) return;
+  const int M = P.M;
+  constexpr int kNLd = TileLoad<4>::kInstr;  // 9 loads per wave per tile
+  constexpr int kAhead = 3;
+  constexpr int kSlots = 18 + 8;             // matrix instructions per tile and wave
+
+  // K fragment (A operand) of k-step ks: token 16 th + l % 16 of the tile,
+  // 16-byte chunk 4 ks + l / 16 -> ka[ks % 2] + (ks / 2) * 1024.
+  int ka[2];
+  {
+    const int r = 16 * th + (lane & 15), lr = r & 7;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      ka[p] = (r >> 3) * kBlkRowStride + lr * 128 + (((4 * p + (lane >> 4)) ^ chunk_swz(lr)) << 4);
+  }
+  // V^T fragment of this wave's d-tile dt (global d-tile 4 wave + dt) and k-step kk:
+  //   v_base[dt % 2] + (2 wave + dt / 2) * 1024 + 2 kk * kBlkRowStride (+ kBlkRowStride)
+  int v_base[2];
+  {
+    const int j16 = lane & 15, g = lane >> 5;
+    const int lr = 4 * g + (j16 >> 2);
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2)
+      v_base[p2] = lr * 128 + (((4 * p2 + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1)) ^ chunk_swz(lr)) << 4) +
+                   8 * (j16 & 1) + wave * 2048;
+  }
+
+  for (int b = b_begin; b <= b_end; ++b) {
+    const int L = ldc(P.seqlens + b);
+    const int npages = L > 0 ? (L + kPage - 1) / kPage : 0;
+    const int p_lo = (b == b_begin) ? page_begin : 0;
+    const int p_hi = (b == b_end) ? page_end : npages;
+    if (p_hi <= p_lo) continue;
+    const int ns0 = ldc(P.num_splits + b), ns1 = ldc(P.num_splits + b + 1);
+    const int split = (b == b_begin) ? split_begin : ns0;
+    const bool single = (ns1 - ns0) == 1;
+    // this lane's query row in the score product (padding rows alias row M - 1)
+    const int qrow = min(16 * rh + (lane & 15), M - 1);
+    const int n_row = P.causal ? L - P.s_q + 1 + (qrow >> P.log2_h) : L;  // keys this row sees
+    const int n_min = P.causal ? L - P.s_q + 1 : L;                      // fewest keys of any row
+    const int tok0 = p_lo * kPage;
+    const int n_tiles = (min(p_hi * kPage, L) - tok0 + kTile - 1) / kTile;
+
+    bf16x8 qf[18];  // B operand: row qrow, dims 32 ks + 8 (l / 16) .. + 7
+    {
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(P.q_lat + (long long)b * M * kDLat), 0, M * kDLat * 2, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(P.q_pe + (long long)b * M * kDRope), 0, M * kDRope * 2, kBufferWord3);
+      const int oq = qrow * (kDLat * 2) + 16 * (lane >> 4), op = qrow * (kDRope * 2) + 16 * (lane >> 4);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+        qf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rq, oq + 64 * ks, 0, 0));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        qf[16 + ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rp, op + 64 * ks, 0, 0));
+    }
+
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    f32x16 acc[4];
+    TileLoad<4> ld;
+    int pid = -1;
+    auto issue_first_tiles = [&]() {
+#pragma unroll 1
+      for (int t = 0; t < min(kAhead, n_tiles); ++t) {
+        if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
+        ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
+#pragma unroll
+        for (int i = 0; i < kNLd; ++i) ld.issue(i);
+      }
+    };
+    __syncthreads();  // every wave is done with the LDS use of the previous piece
+    restart_flag = 0;
+    issue_first_tiles();
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+      m_ref = m_seen;
+      l_run = 0.f;
+      for (int j = 0; j < n_tiles; ++j) {
+        const int later = min(kAhead - 1, n_tiles - 1 - j);
+        if (later >= 2) wait_vmcnt<2 * kNLd>();
+        else if (later == 1) wait_vmcnt<kNLd>();
+        else wait_vmcnt<0>();
+        barrier_keep_loads();
+        const bool more = j + kAhead < n_tiles;
+        if (more) {
+          const int t = j + kAhead;
+          if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
+          ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        MLA_LDS char* tile = lds + (j % kStages) * kTileStageBytes;
+#define MLA_TS_LOAD_SLOT(m) \
+  if ((((m) + 1) * kNLd) / kSlots != ((m) * kNLd) / kSlots && more) ld.issue(((m) * kNLd) / kSlots);
+
+        // ---- S^T = K Q^T for 16 tokens x 16 rows, 576 deep ----
+        f32x4 sc = f32x4{};
+        {
+          bf16x8 kr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kr[i] = lds_read16(tile, ka[i & 1] + (i >> 1) * kBlkBytes);
+#pragma unroll
+          for (int ks = 0; ks < 18; ++ks) {
+            sc = mfma16(kr[ks & 3], qf[ks], sc);
+            if (ks + 4 < 18) kr[ks & 3] = lds_read16(tile, ka[(ks + 4) & 1] + ((ks + 4) >> 1) * kBlkBytes);
+            MLA_TS_LOAD_SLOT(ks)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+
+        // ---- softmax numerators, base 2; sc[i] is token 16 th + 4 (l / 16) + i ----
+        const int t0 = tok0 + j * kTile + 16 * th + 4 * (lane >> 4);
+        if (tok0 + j * kTile + kTile > n_min) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + i >= n_row) sc[i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * P.scale_log2e;  // this wave's 16 tokens of the row
+        m_seen = fmaxf(m_seen, mx);
+        if (pass == 0 && j == 0) {
+          // the reference is the row's max over the whole first tile: both
+          // halves of the tile take it from each other
+          xmax[wave][lane & 15] = mx;
+          barrier_keep_loads();
+          m_ref = fmaxf(mx, xmax[wave ^ 1][lane & 15]);
+        }
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRefSlack) != 0ull) restart_flag = 1;
+        const float msub = m_ref == -INFINITY ? 0.f : m_ref;
+        bf16x4 pw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(sc[i] * P.scale_log2e - msub);
+          l_run += p;
+          pw[i] = (__bf16)p;
+        }
+        // P^T of k-step th, row 16 rh + l % 16, stored in the k order of the
+        // V^T fragments (lane group g of a fragment holds tokens 4 g .. 4 g + 3
+        // and 8 + 4 g .. 8 + 4 g + 3): token t sits at byte
+        // 16 ((t / 4) % 2) + 8 (t / 8) + 2 (t % 4) of the row's 32 bytes
+        *reinterpret_cast<MLA_LDS bf16x4*>(pb + th * 1024 + (16 * rh + (lane & 15)) * 32 +
+                                           ((lane >> 4) & 1) * 16 + (lane >> 5) * 8) = pw;
+        barrier_keep_loads();
+
+        // ---- O^T += V^T P^T: this wave's 128 columns, all 32 rows, 32 tokens ----
+        {
+          bf16x8 pf[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) pf[kk] = lds_read16(pb, kk * 1024 + (lane & 31) * 32 + (lane >> 5) * 16);
+          bf16x4 vr[8][2];
+#pragma unroll
+          for (int it = 0; it < 8; ++it) {  // it = dt * 2 + kk
+            const int dt = it >> 1, kk = it & 1;
+            const int o = v_base[dt & 1] + (dt >> 1) * kBlkBytes + 2 * kk * kBlkRowStride;
+            vr[it][0] = lds_read_tr4(tile, o);
+            vr[it][1] = lds_read_tr4(tile, o + kBlkRowStride);
+          }
+#pragma unroll
+          for (int it = 0; it < 8; ++it) {
+            const int dt = it >> 1, kk = it & 1;
+            acc[dt] = mfma32(cat4(vr[it][0], vr[it][1]), pf[kk], acc[dt]);
+            MLA_TS_LOAD_SLOT(18 + it)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#undef MLA_TS_LOAD_SLOT
+      }
+      wait_vmem_all();
+      __syncthreads();
+      if (restart_flag == 0) break;
+      // a score outgrew the reference: rerun with the row's true max over
+      // both halves of every tile (the next pass cannot restart again)
+      xmax[wave][lane & 15] = m_seen;
+      __syncthreads();
+      m_seen = fmaxf(m_seen, xmax[wave ^ 1][lane & 15]);
+      __syncthreads();
+      restart_flag = 0;
+      issue_first_tiles();
+    }
+
+    // ---- finalise this piece ----
+    // row sums and references of all 32 rows: lane l's output row is l % 32
+    {
+      float lw = l_run;
+      lw += __shfl_xor(lw, 16);
+      lw += __shfl_xor(lw, 32);
+      xl[wave][lane & 15] = lw;
+      xm[rh][lane & 15] = m_ref;  // both waves of a row pair hold the same reference
+    }
+    __syncthreads();
+    const int orow = lane & 31;  // output row of this lane
+    const int ohalf = orow >> 4, on = orow & 15;
+    const float l_tot = xl[2 * ohalf][on] + xl[2 * ohalf + 1][on];
+    const float m_row = xm[ohalf][on];
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float lse_v = l_tot > 0.f ? (m_row + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    const int g = lane >> 5;
+    const int nrows = min(32, M);
+    // acc[dt][v] is column 128 wave + 32 dt + 8 (v / 4) + 4 g + v % 4 of row orow
+    float red;
+    if (single && P.q_lat_lo != nullptr) {
+      // first-order lse correction for the bf16 rounding of q_lat (see mla_decode_kernel)
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(P.q_lat_lo + (long long)b * M * kDLat), 0, M * kDLat * 2, kBufferWord3);
+      const int base = min(orow, M - 1) * (kDLat * 2) + (128 * wave + 4 * g) * 2;
+      float dot = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const u32x2 q2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                         rl, base + (32 * dt + 8 * vq) * 2, 0, 0));
+          const bf16x4 q4 = __builtin_bit_cast(bf16x4, q2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot += acc[dt][4 * vq + e] * (float)q4[e];
+        }
+      red = dot + __shfl_xor(dot, 32);
+    } else {
+      float amax = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(acc[dt][v]));
+      red = fmaxf(amax, __shfl_xor(amax, 32));
+    }
+    xred[wave][orow] = red;
+    __syncthreads();
+    const float r0 = xred[0][orow], r1 = xred[1][orow], r2 = xred[2][orow], r3 = xred[3][orow];
+    // rows leave through LDS as whole 256-byte segments (this wave's columns);
+    // the tile buffers are idle after the piece's last barrier
+    MLA_LDS char* tw = lds + wave * (32 * 272);
+    const int wr = orow * 272 + 8 * g;
+    if (single) {
+      if (P.q_lat_lo != nullptr && l_tot > 0.f) lse_v += P.scale * ((r0 + r1) + (r2 + r3)) * inv_l;
+      const long long rbase = (long long)b * M;
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          P.o_lat + rbase * kDLat, 0, nrows * kDLat * 2, kBufferWord3);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[dt][4 * vq + e] * inv_l);
+          *reinterpret_cast<MLA_LDS bf16x4*>(tw + wr + (32 * dt + 8 * vq) * 2) = w;
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {  // rows 4 k .. 4 k + 3, 256 bytes each
+        const int r = 4 * k + (lane >> 4);
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + r * 272 + (lane & 15) * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, r * (kDLat * 2) + wave * 256 + (lane & 15) * 16, 0, 0);
+      }
+      if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(P.lse + rbase, 0, nrows * 4,
+                                                                            kBufferWord3);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, orow * 4, 0, 0);
+      }
+    } else {
+      const float amax = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+      const float mul = amax > 0.f ? 1.f / amax : 0.f;
+      const long long pbase = (long long)split * M;
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          P.part_o + pbase * kDLat, 0, nrows * kDLat * 2, kBufferWord3);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          _Float16 w0 = (_Float16)(acc[dt][4 * vq + 0] * mul), w1 = (_Float16)(acc[dt][4 * vq + 1] * mul);
+          _Float16 w2 = (_Float16)(acc[dt][4 * vq + 2] * mul), w3 = (_Float16)(acc[dt][4 * vq + 3] * mul);
+          u32x2 w;
+          w[0] = (unsigned)__builtin_bit_cast(unsigned short, w0) | ((unsigned)__builtin_bit_cast(unsigned short, w1) << 16);
+          w[1] = (unsigned)__builtin_bit_cast(unsigned short, w2) | ((unsigned)__builtin_bit_cast(unsigned short, w3) << 16);
+          *reinterpret_cast<MLA_LDS u32x2*>(tw + wr + (32 * dt + 8 * vq) * 2) = w;
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lane >> 4);
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(tw + r * 272 + (lane & 15) * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, r * (kDLat * 2) + wave * 256 + (lane & 15) * 16, 0, 0);
+      }
+      if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(P.part_lse + pbase, 0, nrows * 4,
+                                                                            kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(P.part_scale + pbase, 0, nrows * 4,
+                                                                            kBufferWord3);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, amax * inv_l), rs, orow * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_v), rl, orow * 4, 0, 0);
+      }
+    }
+  }
+}
+
 // Merge split partials: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k,
 // with o_k = scale_k * (fp16 row k).
 // One workgroup per (sequence, 8 rows); 32 threads per row, 16 values each.
@@ -740,7 +1066,7 @@ extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo,
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int grid = R == 1 ? num_slots : ((num_slots + 7) / 8) * 8 * R;
   switch (nw) {
-    case 1: hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(grid), dim3(64), 0, st, P); break;
+    case 1: hipLaunchKernelGGL(mla_decode_tsplit_kernel, dim3(grid), dim3(256), 0, st, P); break;
     case 2: hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(grid), dim3(128), 0, st, P); break;
     default: hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(grid), dim3(256), 0, st, P); break;
   }

@@ -5,6 +5,9 @@
 //  v_mfma_f32_32x32x16_bf16  A: lane l holds row l%32, 8 consecutive k of
 //      group l/32; B: lane l holds column l%32, the same k group; C: lane l,
 //      element v is row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+//  v_mfma_f32_16x16x32_bf16  A: lane l holds row l%16, 8 consecutive k of
+//      group l/16; B: lane l holds column l%16, the same k group; C: lane l,
+//      element i is row 4*(l/16) + i, column l%16.
 //  ds_read_b64_tr_b16  within each 16-lane block, lane j supplies the address
 //      of 4 consecutive 16-bit values in row r0 + j/4 at column c0 + 4*(j%4);
 //      lane i receives column c0 + i of rows r0 .. r0+3. This yields a B (or
@@ -37,6 +40,10 @@ constexpr int kRowBytes = kDRow * 2;     // 1152
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Accumulate into an accumulator pinned to AGPRs. The compiler does not see
