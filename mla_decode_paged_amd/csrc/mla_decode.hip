@@ -263,7 +263,6 @@ void mla_decode_kernel(DecodeParams P) {
     const int p_hi = (b == b_end) ? page_end : npages;
     if (p_hi <= p_lo) continue;
     const int ns0 = ldc(P.num_splits + b), ns1 = ldc(P.num_splits + b + 1);
-    const int pid_first = p_lo < P.max_blocks ? ldc(P.block_table + (long long)b * P.max_blocks + p_lo) : -1;
     const int split = (b == b_begin) ? split_begin : ns0;
     const bool single = (ns1 - ns0) == 1;
     const int n_row = P.causal ? L - P.s_q + 1 + pqj : L;  // keys this row sees
@@ -330,7 +329,6 @@ void mla_decode_kernel(DecodeParams P) {
         const bool more = j + kAhead < n_tiles;
         if (more) {  // tile j + kAhead reuses the buffer of tile j - 1
           const int t = j + kAhead;
-          if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
           ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, pl);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -375,30 +373,37 @@ void mla_decode_kernel(DecodeParams P) {
         const float msub = m_ref == -INFINITY ? 0.f : m_ref;
         float psum = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 8; ++v) {
           sc[v] = fast_exp2(sc[v] * P.scale_log2e - msub);
           psum += sc[v];
         }
-        l_run += psum;
         const bf16x8 pb0 = pack8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
-        const bf16x8 pb1 = pack8(sc[8], sc[9], sc[10], sc[11], sc[12], sc[13], sc[14], sc[15]);
+        bf16x8 pb1;
 
         // ---- O^T += V^T P^T over this tile's 32 tokens, fragments four steps ahead ----
+        // k-step major (it = kk * 16 + dt): the first 16 matrix instructions
+        // need only the first 8 probabilities, and the other 8 are computed
+        // between them
         {
           bf16x4 vr[4][2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {  // step it = dt * 2 + kk
-            const int o = v_base[(i >> 1) & 1] + ((i >> 1) >> 1) * kBlkBytes + 2 * (i & 1) * kBlkRowStride;
+          for (int i = 0; i < 4; ++i) {
+            const int o = v_base[i & 1] + (i >> 1) * kBlkBytes;
             vr[i][0] = lds_read_tr4(tile, o);
             vr[i][1] = lds_read_tr4(tile, o + kBlkRowStride);
           }
 #pragma unroll
           for (int it = 0; it < 32; ++it) {
-            const int dt = it >> 1, kk = it & 1;
+            const int dt = it & 15, kk = it >> 4;
+            if (it == 16) pb1 = pack8(sc[8], sc[9], sc[10], sc[11], sc[12], sc[13], sc[14], sc[15]);
             mfma32_agpr(acc[dt], cat4(vr[it & 3][0], vr[it & 3][1]), kk ? pb1 : pb0);
+            if (it < 8) {
+              sc[8 + it] = fast_exp2(sc[8 + it] * P.scale_log2e - msub);
+              psum += sc[8 + it];
+            }
             if (it + 4 < 32) {
-              const int n = it + 4, ndt = n >> 1;
-              const int o = v_base[ndt & 1] + (ndt >> 1) * kBlkBytes + 2 * (n & 1) * kBlkRowStride;
+              const int n = it + 4, ndt = n & 15, nkk = n >> 4;
+              const int o = v_base[ndt & 1] + (ndt >> 1) * kBlkBytes + 2 * nkk * kBlkRowStride;
               vr[it & 3][0] = lds_read_tr4(tile, o);
               vr[it & 3][1] = lds_read_tr4(tile, o + kBlkRowStride);
             }
@@ -406,7 +411,14 @@ void mla_decode_kernel(DecodeParams P) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        l_run += psum;
 #undef MLA_LOAD_SLOT
+        // page id of the tile the next iteration sets up, fetched here so
+        // that its latency passes under the barrier
+        {
+          const int tn = j + 1 + kAhead;
+          if (tn < n_tiles && (tn & 1) == 0) pid = fetch_pid(P, b, p_lo + (tn >> 1));
+        }
       }
       wait_vmem_all();
       __syncthreads();
