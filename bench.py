@@ -1,7 +1,8 @@
 """Benchmark: one decode step of the paged MLA hot path on one MI355X.
 
 A step is the whole path on one batch: mla_get_metadata, mla_absorb_q,
-mla_decode_paged (split kernel + combine) and mla_up_v. Inputs are seeded
+mla_decode_paged (split kernel + combine) and mla_up_v. The cache append
+(mla_append_kv) is timed on its own after the steps and reported beside them. Inputs are seeded
 synthetic tensors already resident in HBM. To keep the 256 MB Infinity Cache
 from serving repeats, R copies of every input and output rotate, with R times
 the working set above 1 GiB.
@@ -65,6 +66,35 @@ def recorded_traffic(config: str):
     if not m or m.group(1) != config or m.group(3) != h.hexdigest():
         return None
     return int(m.group(2))
+
+
+def time_append(mla, inp, sets, n: int):
+    """The step's cache append (mla_append_kv) on the same workload, after the timed steps:
+    hipEvent time per call over back-to-back calls and its HBM rate (new rows read and written
+    once, plus ints)."""
+    import numpy as np
+    import torch
+
+    from mla_inputs import make_new_rows
+    new = torch.from_numpy(make_new_rows(inp, seed=1).view(np.int16)).view(torch.bfloat16).cuda()
+    for s in sets[:2]:
+        mla.append_kv(new, s["kv"], s["bt"], s["sl"])
+    torch.cuda.synchronize()
+    # The kernel is far shorter than one host-side launch, so the calls are queued behind a
+    # sleeping kernel first: the events then see back-to-back launches, not host latency.
+    torch.cuda._sleep(50_000_000)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        s = sets[i % len(sets)]
+        mla.append_kv(new, s["kv"], s["bt"], s["sl"])
+    e1.record()
+    torch.cuda.synchronize()
+    assert mla.take_device_error() == 0
+    us = e0.elapsed_time(e1) * 1e3 / n
+    nbytes = 2 * inp.b * inp.s_q * 1152 + 4 * inp.b * (1 + inp.s_q)
+    return {"us": round(us, 3), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+            "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 5)}
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -177,6 +207,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert mla.take_device_error() == 0
+    append = time_append(mla, inp, sets, args.steps)
     if args.copy_calibration > 0:  # reads and writes exactly MIB MiB each
         src = torch.ones((args.copy_calibration << 18,), dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -201,6 +232,7 @@ def main():
                    "num_slots": slots, "rotating_copies": R},
         "stage_us": {k: round(v, 3) for k, v in us.items()},
         "decode_us": round(us["decode"], 3),
+        "append_kv": append,
         "latent_kv_TBps": round(work["kv_bytes"] / t_dec / 1e12, 4),
         "decode_TFLOPs": round(tflops, 2),
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -71,6 +71,7 @@ typedef enum {
  * (the kernel then reads zeros instead of the bad address). */
 #define MLA_DEVERR_PAGE_ID 1       /* block_table entry outside [0, num_pages) */
 #define MLA_DEVERR_SEQ_TOO_LONG 2  /* cache_seqlens[b] > max_blocks * 64 */
+#define MLA_DEVERR_SHORT_SEQ 4     /* mla_append_kv: cache_seqlens[b] < s_q */
 
 /* Message for the last non-OK return on this host thread ("" if none). Host. */
 const char* mla_last_error(void);
@@ -176,6 +177,31 @@ int mla_up_v(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int b, in
 int mla_gather_pages(const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
                      int max_blocks, const int32_t* cache_seqlens, int b,
                      const int64_t* row_offsets, uint16_t* out, void* stream);
+
+/* mla_append_kv - write the step's new cache rows into their pages.
+ * The compression stage caches only each token's latent c_KV ("DeepSeek-V3
+ * Multi-head Latent Attention (MLA) 深度工程", section 2.2) with its positional
+ * key k_pos (section 3.2, already rotated here); the paged module of section
+ * 4.3 stores the new token's latent into the paged cache before it attends.
+ * Token t of sequence b is row t % 64 of page block_table[b, t / 64].
+ * cache_seqlens counts the s_q new tokens (as in mla_decode_paged), so new
+ * row j of sequence b becomes token L_b - s_q + j.
+ *
+ * new_rows       bf16 [b, s_q, 576]: c_KV (512 values) then rotated k_pe (64)
+ * kv_cache       bf16 [num_pages, 64, 576], updated in place
+ * block_table    int32 [b, max_blocks]; the caller has mapped the pages the
+ *                new tokens fall in
+ * cache_seqlens  int32 [b]
+ * b >= 1, 1 <= s_q <= 8, num_pages >= 1, max_blocks >= 1.
+ * Only the destination rows change; the copy is bit-exact. A row whose token
+ * index is negative (L_b < s_q: MLA_DEVERR_SHORT_SEQ) or lies past the block
+ * table (MLA_DEVERR_SEQ_TOO_LONG), or whose page id lies outside
+ * [0, num_pages) (MLA_DEVERR_PAGE_ID), is skipped and sets that device error
+ * bit. If two new rows map to the same cache row (a block table that shares
+ * pages between sequences), which one lands is unspecified. */
+int mla_append_kv(const uint16_t* new_rows, uint16_t* kv_cache, int64_t num_pages,
+                  const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                  int b, int s_q, void* stream);
 
 /* Device error word: returns in *bits (host) the MLA_DEVERR_* bits kernels
  * set since the last call, then clears them. Synchronises the device. */

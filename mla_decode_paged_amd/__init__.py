@@ -24,12 +24,15 @@ import os
 import torch
 
 __all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "decode_paged",
-           "up_v", "gather_pages", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
+           "up_v", "gather_pages", "append_kv", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
            "SPLIT_OVERHEAD_FEW_ROWS", "default_split_overhead",
-           "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE"]
+           "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE", "MLA_DEVERR_PAGE_ID",
+           "MLA_DEVERR_SEQ_TOO_LONG", "MLA_DEVERR_SHORT_SEQ"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 PAGE_TOKENS, D_LATENT, D_ROPE, D_ROW, D_NOPE = 64, 512, 64, 576, 128
+# device error bits (MLA_DEVERR_* of include/mla.h)
+MLA_DEVERR_PAGE_ID, MLA_DEVERR_SEQ_TOO_LONG, MLA_DEVERR_SHORT_SEQ = 1, 2, 4
 META_WORDS = 8
 # Fixed cost of one sequence piece in the split plan, in pages: a piece's
 # query loads, first-tile latency, epilogue stores and share of the merge,
@@ -68,6 +71,7 @@ def load():
                                   _P, _P, _P]),
         "mla_up_v": (_I, [_P, _P, _P, _I, _I, _I, _P]),
         "mla_gather_pages": (_I, [_P, _I64, _P, _I, _P, _I, _P, _P, _P]),
+        "mla_append_kv": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _P]),
         "mla_take_device_error": (_I, [ctypes.POINTER(_I)]),
     }
     for name, (res, args) in sig.items():
@@ -208,6 +212,19 @@ def gather_pages(kv_cache, block_table, cache_seqlens, row_offsets, total_rows: 
                                    _ptr(row_offsets, "row_offsets", (torch.int64,), (b,)), _ptr(out, "out"),
                                    _stream()), "mla_gather_pages")
     return out[:total_rows]
+
+
+def append_kv(new_rows, kv_cache, block_table, cache_seqlens):
+    """Write new_rows [b, s_q, 576] into kv_cache in place: new row j of sequence b becomes token
+    cache_seqlens[b] - s_q + j (the lengths count the new tokens)."""
+    if new_rows.dim() != 3 or new_rows.shape[2] != D_ROW:
+        raise MLAError(f"new_rows has shape {tuple(new_rows.shape)}, expected [b, s_q, {D_ROW}]")
+    b, s_q = new_rows.shape[0], new_rows.shape[1]
+    _check(load().mla_append_kv(_ptr(new_rows, "new_rows", _BF16), _ptr(kv_cache, "kv_cache", _BF16),
+                                kv_cache.shape[0], _ptr(block_table, "block_table", _I32), block_table.shape[1],
+                                _ptr(cache_seqlens, "cache_seqlens", _I32, (b,)), b, s_q, _stream()),
+           "mla_append_kv")
+    return kv_cache
 
 
 def take_device_error() -> int:

@@ -985,6 +985,37 @@ __global__ __launch_bounds__(NW * 64) void mla_gather_kernel(DecodeParams P, con
   }
 }
 
+// Cache append: one wave per new row (72 chunks of 16 bytes; lane l copies
+// chunks l and l + 64). Every check is uniform over the wave.
+__global__ __launch_bounds__(64) void mla_append_kernel(const uint16_t* new_rows, uint16_t* kv,
+                                                        long long num_pages, const int32_t* block_table,
+                                                        int max_blocks, const int32_t* seqlens, int s_q) {
+  const int b = blockIdx.x / s_q, j = blockIdx.x % s_q;
+  const int lane = threadIdx.x;
+  const int t = seqlens[b] - s_q + j;  // token index of this new row
+  if (t < 0) {
+    flag_error(MLA_DEVERR_SHORT_SEQ);
+    return;
+  }
+  const int page = t / kPage;
+  if (page >= max_blocks) {
+    flag_error(MLA_DEVERR_SEQ_TOO_LONG);
+    return;
+  }
+  const int pid = block_table[(long long)b * max_blocks + page];
+  if (pid < 0 || pid >= num_pages) {
+    flag_error(MLA_DEVERR_PAGE_ID);
+    return;
+  }
+  const u32x4* src = reinterpret_cast<const u32x4*>(new_rows + ((long long)b * s_q + j) * kDRow);
+  u32x4* dst = reinterpret_cast<u32x4*>(kv + ((long long)pid * kPage + (t % kPage)) * kDRow);
+  constexpr int kChunks = kRowBytes / 16;  // 72
+  const u32x4 v0 = src[lane];
+  const u32x4 v1 = src[min(lane + 64, kChunks - 1)];
+  dst[lane] = v0;
+  if (lane + 64 < kChunks) dst[lane + 64] = v1;
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -1111,6 +1142,25 @@ extern "C" int mla_gather_pages(const uint16_t* kv_cache, int64_t num_pages, con
   // one wave and four waves take different shares of the same load pattern
   hipLaunchKernelGGL(mla_gather_kernel<4>, dim3(max_blocks, b), dim3(256), 0, st, P,
                      reinterpret_cast<const long long*>(row_offsets), out);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess)
+    return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return clear_error();
+}
+
+extern "C" int mla_append_kv(const uint16_t* new_rows, uint16_t* kv_cache, int64_t num_pages,
+                             const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int b,
+                             int s_q, void* stream) {
+  const char* fn = "mla_append_kv";
+  if (!new_rows || !kv_cache || !block_table || !cache_seqlens)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+  if (b < 1) return set_error(MLA_ERR_INVALID_ARG, "%s: b must be >= 1 (got %d)", fn, b);
+  if (s_q < 1 || s_q > 8) return set_error(MLA_ERR_INVALID_ARG, "%s: s_q must be in [1, 8] (got %d)", fn, s_q);
+  if (num_pages < 1 || max_blocks < 1)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: num_pages and max_blocks must be >= 1", fn);
+  if (reinterpret_cast<uintptr_t>(new_rows) % 16 || reinterpret_cast<uintptr_t>(kv_cache) % 16)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: new_rows and kv_cache must be 16-byte aligned", fn);
+  hipLaunchKernelGGL(mla_append_kernel, dim3(b * s_q), dim3(64), 0, static_cast<hipStream_t>(stream), new_rows,
+                     kv_cache, (long long)num_pages, block_table, max_blocks, cache_seqlens, s_q);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return clear_error();

@@ -210,6 +210,13 @@ def make_inputs(config, seed: int = 0, *, trap: bool = False, seqlens=None,
                      q_nope=q_nope, q_pe=q_pe, w_uk=w_uk, w_uv=w_uv, trap_pages=trap_ids)
 
 
+def make_new_rows(inp: MLAInputs, seed: int) -> np.ndarray:
+    """The step's new cache rows for ``inp``: bf16 bits [b, s_q, 576], N(0, 1) like the cache
+    (latent values then the rotated positional key), from their own generator."""
+    rng = np.random.default_rng([seed, 0x6e657752])
+    return _normal_bf16(rng, (inp.b, inp.s_q, D_ROW))
+
+
 def repage(inp: MLAInputs, seed: int) -> MLAInputs:
     """Same logical cache, different physical page placement.
 

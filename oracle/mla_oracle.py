@@ -45,6 +45,32 @@ def token_rows(kv_cache: np.ndarray, block_table: np.ndarray, b: int, n: int) ->
     return kv_cache[block_table[b, t // page], t % page]
 
 
+def append_rows(kv_cache: np.ndarray, block_table: np.ndarray, seqlens: np.ndarray,
+                new_rows: np.ndarray) -> np.ndarray:
+    """Cache after appending the step's new rows (a copy; the input is untouched).
+
+    Each new token's row (latent c^KV and rotated positional key, page
+    "DeepSeek-V3 Multi-head Latent Attention (MLA) 深度工程" sections 2.2 and
+    3.2) is stored into the paged cache before attention (section 4.3). The
+    lengths count the s_q new tokens, so new row j of sequence b is token
+    L_b - s_q + j, which lives at page block_table[b, t // page], slot t % page.
+    Rows whose token index is negative, past the block table, or on a page id
+    outside the cache are skipped (the library flags them as errors).
+    """
+    out = kv_cache.copy()
+    page = kv_cache.shape[1]
+    b_count, s_q = new_rows.shape[0], new_rows.shape[1]
+    for b in range(b_count):
+        for j in range(s_q):
+            t = int(seqlens[b]) - s_q + j
+            if t < 0 or t // page >= block_table.shape[1]:
+                continue
+            pid = int(block_table[b, t // page])
+            if 0 <= pid < kv_cache.shape[0]:
+                out[pid, t % page] = new_rows[b, j]
+    return out
+
+
 def visible_keys(L: int, s_q: int, j: int, causal: bool) -> int:
     """Number of keys query j (0-based among s_q new tokens) may attend to."""
     if not causal:

@@ -310,6 +310,50 @@ def streaming():
         assert abs(lse - (s.max() + math.log(e.sum()))) < 1e-12
 
 
+def append_worked_example():
+    """A hand-worked cache append (page "DeepSeek-V3 Multi-head Latent Attention (MLA) 深度工程",
+    section 4.3: the new token's row goes into its page before attention; the lengths count the
+    new tokens). Pages of 4 rows, rows 3 wide, s_q = 2:
+      sequence 0, L = 5: new rows are tokens 3 and 4 -> page bt[0, 0] = 2 slot 3, page bt[0, 1] = 0 slot 0;
+      sequence 1, L = 2: tokens 0 and 1 -> page bt[1, 0] = 1 slots 0 and 1;
+      sequence 2, L = 1 < s_q: token -1 is skipped, token 0 -> page bt[2, 0] = 3 slot 0;
+      sequence 3, L = 9: tokens 7 (page bt[3, 1] = -1: skipped) and 8 (past the 2-entry table: skipped)."""
+    kv = np.full((4, 4, 3), -1.0)
+    bt = np.array([[2, 0], [1, -1], [3, -1], [0, -1]])
+    L = np.array([5, 2, 1, 9])
+    new = np.arange(4 * 2 * 3, dtype=np.float64).reshape(4, 2, 3) + 100.0
+    out = O.append_rows(kv, bt, L, new)
+    want = np.full((4, 4, 3), -1.0)
+    want[2, 3] = [100, 101, 102]   # seq 0, j 0
+    want[0, 0] = [103, 104, 105]   # seq 0, j 1
+    want[1, 0] = [106, 107, 108]   # seq 1, j 0
+    want[1, 1] = [109, 110, 111]   # seq 1, j 1
+    want[3, 0] = [115, 116, 117]   # seq 2, j 1 (j 0 has token -1)
+    assert np.array_equal(out, want)
+    assert np.array_equal(kv, np.full((4, 4, 3), -1.0))  # the input is not modified
+
+
+def append_round_trip():
+    """Reading the cache back through the pinned token gather: the last s_q tokens of every
+    sequence are the new rows, every earlier token and every other cache row is unchanged."""
+    rng = np.random.default_rng(21)
+    page, P, s_q = 64, 40, 3
+    kv = rng.standard_normal((P, page, 5))
+    L = np.array([3, 64, 65, 130, 1000 % 640])
+    bt = rng.permutation(P)[:5 * 8].reshape(5, 8)
+    new = rng.standard_normal((5, s_q, 5))
+    out = O.append_rows(kv, bt, L, new)
+    touched = np.zeros((P, page), dtype=bool)
+    for b in range(5):
+        before, after = O.token_rows(kv, bt, b, int(L[b])), O.token_rows(out, bt, b, int(L[b]))
+        assert np.array_equal(after[L[b] - s_q:], new[b])
+        assert np.array_equal(after[:L[b] - s_q], before[:L[b] - s_q])
+        for t in range(L[b] - s_q, L[b]):
+            touched[bt[b, t // page], t % page] = True
+    assert np.array_equal(out[~touched], kv[~touched])
+
+
 ALL_PINS = [brute_force_tiny, brute_force_real_dims, sdpa_library, absorb_identity, up_v_identity,
             rows_sum_to_one, page_permutation, gather_indexing, zero_query, single_token,
-            identical_rows, causal_reduction, split_merge, streaming]
+            identical_rows, causal_reduction, split_merge, streaming, append_worked_example,
+            append_round_trip]

@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for fn in ("mla_get_metadata", "mla_absorb_q", "mla_decode_paged", "mla_up_v", "mla_gather_pages",
+    for fn in ("mla_get_metadata", "mla_absorb_q", "mla_decode_paged", "mla_up_v", "mla_gather_pages", "mla_append_kv",
                "mla_last_error", "mla_num_slots", "mla_workspace_bytes", "mla_take_device_error"):
         assert fn in names
 
@@ -100,6 +100,13 @@ def test_other_calls_reject(lib):
     assert lib.mla_up_v(FAKE, FAKE, FAKE, 2, 0, 16, None) == INVALID
     assert lib.mla_gather_pages(FAKE, 0, FAKE, 4, FAKE, 2, FAKE, FAKE, None) == INVALID
     assert lib.mla_gather_pages(FAKE, 4, FAKE, 4, FAKE, 2, None, FAKE, None) == INVALID
+    assert lib.mla_append_kv(None, FAKE, 4, FAKE, 4, FAKE, 2, 1, None) == INVALID
+    assert lib.mla_append_kv(FAKE, FAKE, 4, FAKE, 4, None, 2, 1, None) == INVALID
+    assert lib.mla_append_kv(FAKE, FAKE, 4, FAKE, 4, FAKE, 0, 1, None) == INVALID
+    assert lib.mla_append_kv(FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 9, None) == INVALID
+    assert lib.mla_append_kv(FAKE, FAKE, 0, FAKE, 4, FAKE, 2, 1, None) == INVALID
+    assert lib.mla_append_kv(FAKE, FAKE, 4, FAKE, 0, FAKE, 2, 1, None) == INVALID
+    assert lib.mla_append_kv(ctypes.c_void_p((1 << 20) + 8), FAKE, 4, FAKE, 4, FAKE, 2, 1, None) == INVALID
     assert lib.mla_num_slots(2, 1, 16, None) == INVALID
     assert lib.mla_take_device_error(None) == INVALID
     assert lib.mla_last_error().decode() != ""

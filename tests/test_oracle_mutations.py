@@ -97,7 +97,41 @@ def _stream_no_keep(s, values):
     return acc, m + np.log(l)
 
 
+def _append_with(token_of):
+    def bad(kv, bt, L, new):
+        out = kv.copy()
+        page = kv.shape[1]
+        for b in range(new.shape[0]):
+            for j in range(new.shape[1]):
+                t = token_of(int(L[b]), new.shape[1], j)
+                if t < 0 or t // page >= bt.shape[1]:
+                    continue
+                pid = int(bt[b, t // page])
+                if 0 <= pid < kv.shape[0]:
+                    out[pid, t % page] = new[b, j]
+        return out
+    return bad
+
+
+def _append_page_slot_swapped(kv, bt, L, new):
+    out = kv.copy()
+    page = kv.shape[1]
+    for b in range(new.shape[0]):
+        for j in range(new.shape[1]):
+            t = int(L[b]) - new.shape[1] + j
+            if t < 0 or t % page >= bt.shape[1] or t // page >= page:
+                continue
+            pid = int(bt[b, t % page])
+            if 0 <= pid < kv.shape[0]:
+                out[pid, t // page] = new[b, j]
+    return out
+
+
 MUTATIONS = {
+    "append_off_by_one": ("append_rows", _append_with(lambda L, s_q, j: L - s_q + j + 1)),
+    "append_reversed_rows": ("append_rows", _append_with(lambda L, s_q, j: L - 1 - j)),
+    "append_at_start": ("append_rows", _append_with(lambda L, s_q, j: j)),
+    "append_page_slot_swapped": ("append_rows", _append_page_slot_swapped),
     "rows_ignore_block_table": ("token_rows", _rows_no_block_table),
     "rows_slot_shift": ("token_rows", _rows_slot_shift),
     "rows_slot_reversed": ("token_rows", _rows_slot_reversed),
@@ -121,7 +155,8 @@ MUTATIONS = {
 }
 
 # cheap pins first: the first failure ends a mutation's run
-ORDER = [pins.split_merge, pins.streaming, pins.gather_indexing, pins.rows_sum_to_one, pins.zero_query,
+ORDER = [pins.append_worked_example, pins.append_round_trip,
+         pins.split_merge, pins.streaming, pins.gather_indexing, pins.rows_sum_to_one, pins.zero_query,
          pins.single_token, pins.identical_rows, pins.causal_reduction, pins.up_v_identity,
          pins.absorb_identity, pins.page_permutation, pins.sdpa_library, pins.brute_force_tiny,
          pins.brute_force_real_dims]
