@@ -82,7 +82,7 @@ def time_append(mla, inp, sets, n: int):
     torch.cuda.synchronize()
     # The kernel is far shorter than one host-side launch, so the calls are queued behind a
     # sleeping kernel first: the events then see back-to-back launches, not host latency.
-    torch.cuda._sleep(50_000_000)
+    torch.cuda._sleep(10_000_000)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n):
