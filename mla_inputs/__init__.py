@@ -49,8 +49,11 @@ CONFIGS: dict[str, dict] = {
                          seqlens=("lognormal", 8192, 1.0, 1, 65536)),
     # two query tokens per sequence under a causal mask (speculative verify)
     "multi_token": dict(b=128, h=128, s_q=2, causal=True, seqlens=("all", 4096)),
+    # speculative verify with a longer draft: 8 query tokens per sequence
+    # (1024 query rows), causal, lengths uniform in [256, 4096]
+    "spec_verify": dict(b=32, h=128, s_q=8, causal=True, seqlens=("uniform", 256, 4096)),
 }
-CONFIG_ORDER = ["tiny", "tp_share", "full_heads", "long_context", "multi_token"]
+CONFIG_ORDER = ["tiny", "tp_share", "full_heads", "long_context", "multi_token", "spec_verify"]
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -41,6 +41,8 @@ def test_tiny_config_poisoned(gpu_lib):
     ([1025, 1024, 5], 2, 64, True),
     ([700, 90], 4, 32, True),                      # 128 rows
     ([333, 2000], 4, 128, True),                   # 512 rows: four row blocks
+    ([8, 100, 1031], 8, 128, True),                # 1024 rows: eight row blocks, the longest draft
+    ([9, 64, 700], 8, 16, True),                   # 128 rows of 8 query tokens
 ])
 def test_edge_shapes(gpu_lib, seqlens, s_q, h, causal):
     inp = make_inputs("tiny", seed=5, seqlens=seqlens, s_q=s_q, h=h, causal=causal, trap=True)
@@ -68,6 +70,7 @@ FULL = {
     "full_heads": ([0, 5, 42, 77, 127], [0, 64, 127]),
     "long_context": (None, [0, 100]),
     "multi_token": ([0, 63, 127], [0, 127]),
+    "spec_verify": ([0, 17, 31], [0, 77, 127]),
 }
 
 
