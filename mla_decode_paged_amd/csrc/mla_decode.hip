@@ -877,82 +877,85 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
 
 // Merge split partials: lse = ln sum_k exp(lse_k), o = sum_k exp(lse_k - lse) o_k,
 // with o_k = scale_k * (fp16 row k).
-// One workgroup per (sequence, 8 rows); 32 threads per row, 16 values each.
+// One workgroup per (sequence, 16 rows); 16 threads per row, each holding 32
+// values as four 16-byte chunks (chunk t + 16 q of the row).
 __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
   const int b = blockIdx.x;
-  const int row = blockIdx.y * 8 + (threadIdx.x >> 5);
-  const int t = threadIdx.x & 31;
+  const int row = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
   if (row >= P.M) return;
   const int ns0 = P.num_splits[b], n = P.num_splits[b + 1] - ns0;
   if (n == 1) return;
   const long long orow = (long long)b * P.M + row;
-  uint16_t* out = P.o_lat + orow * kDLat;
+  u32x4* out = reinterpret_cast<u32x4*>(P.o_lat + orow * kDLat) + t;
   if (n == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint2 z = {0u, 0u};
-      *reinterpret_cast<uint2*>(out + 128 * q + 4 * t) = z;
-    }
+    for (int q = 0; q < 4; ++q) out[16 * q] = u32x4{};
     if (t == 0) P.lse[orow] = -INFINITY;
     return;
   }
   // Streaming merge over the pieces, four at a time with every load of a
   // group issued before any is used: running max m, weights exp(lse_k - m).
   float mx = -INFINITY, wsum = 0.f;
-  f32x4 o[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+  float o[32];
+#pragma unroll
+  for (int v = 0; v < 32; ++v) o[v] = 0.f;
   for (int k0 = 0; k0 < n; k0 += 4) {
     float lk[4], sk[4];
-    u32x2 src[4][4];  // 4 fp16 values each
+    u32x4 src[4][4];  // 8 fp16 values each
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const long long prow = (long long)(ns0 + min(k0 + i, n - 1)) * P.M + row;  // short groups repeat the last piece
       lk[i] = k0 + i < n ? P.part_lse[prow] : -INFINITY;
       sk[i] = P.part_scale[prow];
-      const u32x2* sp = reinterpret_cast<const u32x2*>(P.part_o + prow * kDLat) + t;
+      const u32x4* sp = reinterpret_cast<const u32x4*>(P.part_o + prow * kDLat) + t;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) src[i][q] = sp[32 * q];
+      for (int q = 0; q < 4; ++q) src[i][q] = sp[16 * q];
     }
     const float m_new = fmaxf(fmaxf(mx, fmaxf(lk[0], lk[1])), fmaxf(lk[2], lk[3]));
     if (m_new == -INFINITY) continue;  // nothing visible yet (uniform over the row's threads)
     const float alpha = fast_exp2((mx - m_new) * 1.4426950408889634f);  // 0 when mx = -inf
     wsum *= alpha;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] *= alpha;
+    for (int v = 0; v < 32; ++v) o[v] *= alpha;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float w = fast_exp2((lk[i] - m_new) * 1.4426950408889634f);  // 0 for padding entries
       wsum += w;
       const float ws = w * sk[i];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const unsigned lo16 = src[i][q][0], hi16 = src[i][q][1];
-        o[q][0] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(lo16 & 0xffffu));
-        o[q][1] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(lo16 >> 16));
-        o[q][2] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(hi16 & 0xffffu));
-        o[q][3] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(hi16 >> 16));
-      }
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h2 = 0; h2 < 4; ++h2) {
+          const unsigned u = src[i][q][h2];
+          o[8 * q + 2 * h2] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(u & 0xffffu));
+          o[8 * q + 2 * h2 + 1] += ws * (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> 16));
+        }
     }
     mx = m_new;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float dot = 0.f;  // q_lo . o_lat for the first-order lse correction (see the decode epilogue)
-  const uint16_t* qlo = P.q_lat_lo != nullptr ? P.q_lat_lo + orow * kDLat : nullptr;
+  const u32x4* qlo = P.q_lat_lo != nullptr ? reinterpret_cast<const u32x4*>(P.q_lat_lo + orow * kDLat) + t : nullptr;
+  u32x4 q8[4];
+  if (qlo != nullptr) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) q8[q] = qlo[16 * q];
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    bf16x4 w;
-    w[0] = (__bf16)(o[q][0] * inv);
-    w[1] = (__bf16)(o[q][1] * inv);
-    w[2] = (__bf16)(o[q][2] * inv);
-    w[3] = (__bf16)(o[q][3] * inv);
-    *reinterpret_cast<bf16x4*>(out + 128 * q + 4 * t) = w;
-    if (qlo != nullptr) {
-      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(qlo + 128 * q + 4 * t);
+    bf16x8 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dot += o[q][e] * inv * (float)q4[e];
+    for (int e = 0; e < 8; ++e) w[e] = (__bf16)(o[8 * q + e] * inv);
+    out[16 * q] = __builtin_bit_cast(u32x4, w);
+    if (qlo != nullptr) {
+      const bf16x8 qv = __builtin_bit_cast(bf16x8, q8[q]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += o[8 * q + e] * inv * (float)qv[e];
     }
   }
 #pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);  // the row's 32 threads
+  for (int m = 8; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);  // the row's 16 threads
   if (t == 0)
     P.lse[orow] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 + P.scale * dot : -INFINITY;
 }
@@ -1115,7 +1118,7 @@ extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo,
   }
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: decode launch failed: %s", fn, hipGetErrorString(e));
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(b, (M + 7) / 8), dim3(256), 0, st, P);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(b, (M + 15) / 16), dim3(256), 0, st, P);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: combine launch failed: %s", fn, hipGetErrorString(e));
   return clear_error();
