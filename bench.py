@@ -7,6 +7,12 @@ synthetic tensors already resident in HBM. To keep the 256 MB Infinity Cache
 from serving repeats, R copies of every input and output rotate, with R times
 the working set above 1 GiB.
 
+`value` is the wall time per step with each step replayed from a HIP graph
+(one graph per rotating input set, recorded through torch's graph capture on
+the library's stream), so no host launch gap sits between the kernels of a
+step; `eager_us_per_step` is the same steps launched eagerly, whose per-call
+hipEvents give `stage_us` and the decode call's roofline.
+
 Prints one JSON line (rank 0, N = 1). Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config full_heads]
 """
@@ -131,6 +137,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the steps as eager launches only (value = eager wall time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy (torch.neg) of MIB MiB so that "
                          "hardware byte counters can be scaled against a kernel of known traffic")
@@ -173,7 +181,6 @@ def main():
             o=torch.empty((inp.b, inp.s_q, inp.h, 128), dtype=torch.bfloat16, device="cuda")))
     slots = mla.num_slots(inp.b, inp.s_q, inp.h)
     ws = torch.empty((mla.workspace_bytes(inp.b, inp.s_q, inp.h, slots),), dtype=torch.uint8, device="cuda")
-    metas = [mla.get_metadata(s["sl"], slots, s_q=inp.s_q, h=inp.h) for s in sets]
 
     ev = {k: [] for k in ("meta", "absorb", "decode", "up_v")}
 
@@ -207,6 +214,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert mla.take_device_error() == 0
+    us_step_eager = wall / args.steps * 1e6
+    # The same steps replayed from HIP graphs, one per rotating input set:
+    # each step's launches are recorded once, so a replay has no host launch
+    # gaps between its kernels. The per-call events above give the stages.
+    us_step_graph = None
+    if not args.no_graph:
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r, False)
+            graphs.append(g)
+        for i in range(max(args.warmup, R)):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        us_step_graph = (time.perf_counter() - t0) / args.steps * 1e6
+        assert mla.take_device_error() == 0
+        del graphs
     append = time_append(mla, inp, sets, args.steps)
     if args.copy_calibration > 0:  # reads and writes exactly MIB MiB each
         src = torch.ones((args.copy_calibration << 18,), dtype=torch.float32, device="cuda")
@@ -216,7 +245,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     us = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in ev.items()}
-    us_step = wall / args.steps * 1e6
+    us_step = us_step_graph if us_step_graph is not None else us_step_eager
 
     t_dec = us["decode"] * 1e-6
     achieved = work["bytes"] / t_dec / 1e9
@@ -230,6 +259,8 @@ def main():
                                f"seqlens={cfg['seqlens']} sum_L={int(inp.seqlens.sum())} page=64 row=576 bf16 "
                                f"seed={args.seed}",
                    "num_slots": slots, "rotating_copies": R},
+        "step_mode": "hip_graph" if us_step_graph is not None else "eager",
+        "eager_us_per_step": round(us_step_eager, 3),
         "stage_us": {k: round(v, 3) for k, v in us.items()},
         "decode_us": round(us["decode"], 3),
         "append_kv": append,
