@@ -7,7 +7,9 @@
 // and 3.1), an exact softmax kept in streaming form (the same page's section
 // 4.1 recurrence), o_lat[r] = sum_t p_t c_t and lse[r].
 //
-// How it maps onto MI355X (one workgroup = NW wavefronts, 32 query rows each):
+// How it maps onto MI355X (mla_decode_kernel: one workgroup = NW wavefronts,
+// 32 query rows each; with at most 32 rows, mla_decode_tsplit_kernel below
+// splits each tile's tokens over four wavefronts instead):
 //  * Page loader. A page is 64 rows x 1152 contiguous bytes. It is copied
 //    straight from HBM into LDS with 16-byte direct-to-LDS loads
 //    (global_load_lds_dwordx4), one wave instruction per 8-row x 128-byte
@@ -17,12 +19,13 @@
 //    work. Inside a block the 16-byte chunks of row r are XOR-permuted and
 //    each 8-row block row is shifted by 32 bytes; with that, the K-fragment
 //    reads of QK^T (32 rows x 16 bytes) and the transposed V reads of PV
-//    (4 rows x 32 bytes per 16 lanes) both hit 64 distinct banks. Two page
-//    buffers alternate, so the next page streams in while the current one is
-//    multiplied; this is the double buffer of the SC11 note's Page Attention
-//    figure, done by the CU's own load path instead of separate DMA engines.
-//    Tokens past the cache length and bad page ids load a zero row, so NaN or
-//    stale data never reach LDS.
+//    (4 rows x 32 bytes per 16 lanes) both hit 64 distinct banks. Four
+//    32-token tile buffers rotate with three tiles in flight, so later tiles
+//    stream in while the current one is multiplied; this is the double buffer
+//    of the SC11 note's Page Attention figure, done by the CU's own load path
+//    instead of separate DMA engines. Rows past the cache length repeat the
+//    page's last cached row (finite, and masked to zero weight) and bad page
+//    ids read a zero page, so NaN or stale data never reach LDS.
 //  * QK^T on the matrix cores, transposed: S^T[token, row] = K Q^T with K
 //    (the page rows) as the A operand read from LDS and Q as the B operand
 //    held in VGPRs for the whole piece. Each lane then owns 16 scores of ONE
@@ -40,8 +43,9 @@
 //    reference makes the workgroup recompute the piece with a larger one.
 //  * Split-KV: the planner hands each workgroup slot a contiguous run of
 //    pages (possibly spanning several sequences). A sequence held by one slot
-//    is finalised in place; otherwise each piece writes an fp32 partial (O/l,
-//    lse) and mla_combine merges them by lse rescaling.
+//    is finalised in place; otherwise each piece writes a partial row as fp16
+//    divided by its largest magnitude, with that scale and its lse, and
+//    mla_combine_kernel merges the pieces by lse rescaling.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
