@@ -8,7 +8,11 @@
 // to the attention output instead of to every cached token (section 2.2).
 //
 // Each workgroup computes one head's 128-row x NT-column output tile (four
-// waves of 32 rows) with 32x32x16 bf16 MFMAs, as the transposed product
+// waves of 32 rows). The tiles of one head are consecutive workgroups on one
+// XCD (workgroup ids go round-robin over the 8 XCDs), so the A rows and the
+// weight columns that several tiles of the head read come from that XCD's L2
+// after the first read. The tile is computed with 32x32x16 bf16 MFMAs, as the
+// transposed product
 // C^T = W^T A^T. The weight tile W[i][0:K][n0:n0+NT] is staged in LDS once
 // and read back transposed as the A operand; each lane's B operand (8
 // consecutive k of one row of A) is 16 contiguous bytes of that row, loaded
@@ -38,7 +42,13 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
   constexpr int kKS = K / 16;                   // k-steps
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   MLA_LDS char* lds = (MLA_LDS char*)(smem);
-  const int n0 = blockIdx.x * NT, r0 = blockIdx.y * kGemmRows, head = blockIdx.z;
+  // workgroup -> (head, row block, column tile): head = 8 j + (id % 8) for
+  // the j-th run of tiles on XCD id % 8
+  constexpr int kTilesN = N / NT;
+  const int per_head = kTilesN * ((R + kGemmRows - 1) / kGemmRows);
+  const int idx = blockIdx.x >> 3, head = (idx / per_head) * 8 + (blockIdx.x & 7), inner = idx % per_head;
+  if (head >= h) return;
+  const int n0 = (inner % kTilesN) * NT, r0 = (inner / kTilesN) * kGemmRows;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, g = lane >> 5, j16 = lane & 15;
 
@@ -154,12 +164,13 @@ extern "C" int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16
   // (14.4 against 16.5 us).
   const int rb = (R + kGemmRows - 1) / kGemmRows;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int hg = (h + 7) / 8 * 8;
   if (h <= 32)
-    hipLaunchKernelGGL((head_gemm_kernel<kDNope, kDLat, 64>), dim3(kDLat / 64, rb, h), dim3(256), 0, st, q_nope,
+    hipLaunchKernelGGL((head_gemm_kernel<kDNope, kDLat, 64>), dim3(kDLat / 64 * rb * hg), dim3(256), 0, st, q_nope,
                        w_uk, q_lat, q_lat_lo, R, h);
   else
-    hipLaunchKernelGGL((head_gemm_kernel<kDNope, kDLat, 128>), dim3(kDLat / 128, rb, h), dim3(256), 0, st, q_nope,
-                       w_uk, q_lat, q_lat_lo, R, h);
+    hipLaunchKernelGGL((head_gemm_kernel<kDNope, kDLat, 128>), dim3(kDLat / 128 * rb * hg), dim3(256), 0, st,
+                       q_nope, w_uk, q_lat, q_lat_lo, R, h);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return clear_error();
@@ -176,11 +187,12 @@ extern "C" int mla_up_v(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o
   // as in mla_absorb_q: narrower tiles with few heads (h = 32: 7.3 -> 6.9 us), not with 128 (11.6 against 16.7 us)
   const int rb = (R + kGemmRows - 1) / kGemmRows;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int hg = (h + 7) / 8 * 8;
   if (h <= 32)
-    hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 32>), dim3(kDNope / 32, rb, h), dim3(256), 0, st, o_lat,
+    hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 32>), dim3(kDNope / 32 * rb * hg), dim3(256), 0, st, o_lat,
                        w_uv, o, static_cast<uint16_t*>(nullptr), R, h);
   else
-    hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 64>), dim3(kDNope / 64, rb, h), dim3(256), 0, st, o_lat,
+    hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 64>), dim3(kDNope / 64 * rb * hg), dim3(256), 0, st, o_lat,
                        w_uv, o, static_cast<uint16_t*>(nullptr), R, h);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
