@@ -180,6 +180,9 @@ def main():
             lse=torch.empty((inp.b, inp.s_q, inp.h), dtype=torch.float32, device="cuda"),
             o=torch.empty((inp.b, inp.s_q, inp.h, 128), dtype=torch.bfloat16, device="cuda")))
     slots = mla.num_slots(inp.b, inp.s_q, inp.h)
+    for s in sets:
+        s["meta"] = torch.empty((slots, mla.META_WORDS), dtype=torch.int32, device="cuda")
+        s["ns"] = torch.empty((inp.b + 1,), dtype=torch.int32, device="cuda")
     ws = torch.empty((mla.workspace_bytes(inp.b, inp.s_q, inp.h, slots),), dtype=torch.uint8, device="cuda")
 
     ev = {k: [] for k in ("meta", "absorb", "decode", "up_v")}
@@ -189,7 +192,7 @@ def main():
         e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
         if timed:
             e[0].record()
-        meta, ns = mla.get_metadata(s["sl"], slots, s_q=inp.s_q, h=inp.h)
+        meta, ns = mla.get_metadata(s["sl"], slots, s_q=inp.s_q, h=inp.h, out=(s["meta"], s["ns"]))
         if timed:
             e[1].record()
         mla.absorb_q(s["q_nope"], s["w_uk"], out=(s["q_lat"], s["q_lo"]))

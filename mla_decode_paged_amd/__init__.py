@@ -131,18 +131,22 @@ def default_split_overhead(s_q: int, h: int) -> int:
 
 
 def get_metadata(cache_seqlens: torch.Tensor, slots: int | None = None, s_q: int = 1, h: int = 128,
-                 split_overhead: int | None = None):
+                 split_overhead: int | None = None, out=None):
     """Split-KV plan: (tile_meta int32 [slots, 8], num_splits int32 [b + 1])."""
     b = cache_seqlens.numel()
     if split_overhead is None:
         split_overhead = default_split_overhead(s_q, h)
     if slots is None:
-        slots = num_slots(b, s_q, h)
+        slots = num_slots(b, s_q, h) if out is None else out[0].shape[0]
     dev = cache_seqlens.device
-    tile_meta = torch.empty((slots, META_WORDS), dtype=torch.int32, device=dev)
-    num_splits = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    if out is None:
+        tile_meta = torch.empty((slots, META_WORDS), dtype=torch.int32, device=dev)
+        num_splits = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    else:
+        tile_meta, num_splits = out
     _check(load().mla_get_metadata(_ptr(cache_seqlens, "cache_seqlens", _I32), b, slots, split_overhead,
-                                   _ptr(tile_meta, "tile_meta"), _ptr(num_splits, "num_splits"), _stream()),
+                                   _ptr(tile_meta, "tile_meta", _I32, (slots, META_WORDS)),
+                                   _ptr(num_splits, "num_splits", _I32, (b + 1,)), _stream()),
            "mla_get_metadata")
     return tile_meta, num_splits
 
