@@ -68,3 +68,26 @@ def test_plan_bit_exact(gpu_lib, seqlens, slots, F):
     ref_meta, ref_ns, _ = SP.plan(seqlens, slots, F)
     assert np.array_equal(ns.cpu().numpy(), ref_ns)
     assert np.array_equal(meta.cpu().numpy(), ref_meta)
+
+
+def test_plan_into_given_buffers(gpu_lib):
+    """get_metadata(out=...) writes the same plan into caller buffers (overwriting what they held)
+    and rejects buffers of the wrong shape or dtype before any launch."""
+    mla = gpu_lib
+    seqlens = [3000, 0, 64, 700, 1]
+    slots = 9
+    sl = torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    meta = torch.full((slots, mla.META_WORDS), -7, dtype=torch.int32, device="cuda")
+    ns = torch.full((len(seqlens) + 1,), -7, dtype=torch.int32, device="cuda")
+    got_meta, got_ns = mla.get_metadata(sl, slots, split_overhead=2, out=(meta, ns))
+    assert got_meta.data_ptr() == meta.data_ptr() and got_ns.data_ptr() == ns.data_ptr()
+    ref_meta, ref_ns, _ = SP.plan(seqlens, slots, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(meta.cpu().numpy(), ref_meta)
+    assert np.array_equal(ns.cpu().numpy(), ref_ns)
+    bad = [(torch.empty((slots, 4), dtype=torch.int32, device="cuda"), ns),
+           (meta, torch.empty((len(seqlens),), dtype=torch.int32, device="cuda")),
+           (meta.to(torch.int64), ns)]
+    for out in bad:
+        with pytest.raises(mla.MLAError):
+            mla.get_metadata(sl, slots, split_overhead=2, out=out)
