@@ -87,3 +87,22 @@ def test_full_size_sampled(gpu_lib, cfg):
     compare(res, ref, seqs, heads, label=cfg)
     assert np.isfinite(res["o_lat"]).all() and np.isfinite(res["lse"]).all()
     assert gpu_lib.take_device_error() == 0
+
+
+@pytest.mark.parametrize("h", [16, 128])
+def test_maximum_batch(gpu_lib, h):
+    """b = MLA_MAX_BATCH (8192) short sequences, some empty: row and page offsets at the far end of
+    every tensor, and 64 row blocks in the projections. Sampled sequences include both ends."""
+    rng = np.random.default_rng(21)
+    seqlens = rng.integers(0, 151, 8192)
+    seqlens[[1, 4097, 8190]] = 0
+    inp = make_inputs("tiny", seed=21, seqlens=seqlens.tolist(), h=h)
+    seqs = sorted({0, 1, 2, 4096, 4097, 8189, 8190, 8191} | set(rng.integers(0, 8192, 4).tolist()))
+    heads = [0, h // 2 + 1, h - 1]
+    say("max batch h", h, "sum L", int(inp.seqlens.sum()), "seqs", seqs)
+    res = host(run_path(gpu_lib, DevInputs(inp)))
+    ref = O.decode_naive_inputs(inp, seqs=seqs, heads=heads)
+    compare(res, ref, seqs, heads, label=f"max batch h={h}")
+    empty = inp.seqlens <= 0
+    assert (res["lse"][empty] == -np.inf).all() and not res["o_lat"][empty].any()
+    assert gpu_lib.take_device_error() == 0
