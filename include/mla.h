@@ -204,7 +204,10 @@ int mla_append_kv(const uint16_t* new_rows, uint16_t* kv_cache, int64_t num_page
                   int b, int s_q, void* stream);
 
 /* Device error word: returns in *bits (host) the MLA_DEVERR_* bits kernels
- * set since the last call, then clears them. Synchronises the device. */
+ * set since the last call, then clears them. Synchronises the device. The
+ * read and the clear are two copies: a bit set by a kernel that another host
+ * thread launches between them is lost, so call it while no other thread
+ * launches work on the device. */
 int mla_take_device_error(int* bits /* host out */);
 
 #ifdef __cplusplus
