@@ -144,8 +144,8 @@ def main():
                          "hardware byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path does not shard "
-              "across GPUs in this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library runs on one "
+              "GPU and does not shard the decode across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
