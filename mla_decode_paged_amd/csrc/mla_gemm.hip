@@ -28,6 +28,7 @@ namespace mla {
 
 constexpr int kGemmRows = 128;  // rows per workgroup: 4 waves x 32
 constexpr int kBufferWord3G = 0x00020000;  // raw buffer resource: dword data, bounds-checked
+constexpr int kStoreNT = 2;                 // buffer store cache policy: non-temporal
 
 template <int K, int N, int NT>
 __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
@@ -111,7 +112,9 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
       *reinterpret_cast<MLA_LDS bf16x4*>(lds + off) = hi;
       if (out_lo != nullptr) *reinterpret_cast<MLA_LDS bf16x4*>(lds + kOBytes + off) = lo;
     }
-  // each wave stores its own 32 rows (only its own LDS rows are read back)
+  // each wave stores its own 32 rows (only its own LDS rows are read back);
+  // the stores are non-temporal (cache policy nt): the outputs stream out,
+  // and nothing in this kernel reads them back
   constexpr int kLanesPerRow = NT * 2 / 16;
   constexpr int kRowsPerInstr = 64 / kLanesPerRow;
   const int rr = lane / kLanesPerRow, ch = lane % kLanesPerRow;
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
   for (int k = 0; k < 32; k += kRowsPerInstr) {
     const int lr = wave * 32 + k + rr;
     const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(lds + lr * kOPitch + ch * 16);
-    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (unsigned)(lr * row_stride) + ch * 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (unsigned)(lr * row_stride) + ch * 16, 0, kStoreNT);
   }
   if (out_lo != nullptr) {
     const __amdgpu_buffer_rsrc_t rlo = __builtin_amdgcn_make_buffer_rsrc(
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
     for (int k = 0; k < 32; k += kRowsPerInstr) {
       const int lr = wave * 32 + k + rr;
       const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(lds + kOBytes + lr * kOPitch + ch * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(v, rlo, (unsigned)(lr * row_stride) + ch * 16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rlo, (unsigned)(lr * row_stride) + ch * 16, 0, kStoreNT);
     }
   }
 }
