@@ -883,10 +883,21 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
 // with o_k = scale_k * (fp16 row k).
 // One workgroup per (sequence, 16 rows); 16 threads per row, each holding 32
 // values as four 16-byte chunks (chunk t + 16 q of the row).
+// Split-combine: one workgroup of four waves per (sequence, 4 R rows); a wave
+// merges R rows, each spread over 64 / R lanes that hold R 16-byte chunks of
+// it (chunk t + (64 / R) q of the row's 64), and keeps 16 / R pieces of every
+// row in flight per group. R = 4 suits sequences cut into a few pieces
+// (every lane has 16 loads in flight across its rows); R = 1 gives a
+// sequence cut into many pieces 4x more waves, so each row's chain of
+// dependent groups is 4x shorter.
+template <int R>
 __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
+  constexpr int kLanesPerRow = 64 / R;
+  constexpr int kGroup = 16 / R;  // pieces of every row whose loads are in flight together
   const int b = blockIdx.x;
-  const int row = blockIdx.y * 16 + (threadIdx.x >> 4);
-  const int t = threadIdx.x & 15;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.y * (4 * R) + wave_id_uniform() * R + lane / kLanesPerRow;
+  const int t = lane % kLanesPerRow;
   if (row >= P.M) return;
   const int ns0 = P.num_splits[b], n = P.num_splits[b + 1] - ns0;
   if (n == 1) return;
@@ -894,41 +905,60 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
   u32x4* out = reinterpret_cast<u32x4*>(P.o_lat + orow * kDLat) + t;
   if (n == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[16 * q] = u32x4{};
+    for (int q = 0; q < R; ++q) out[kLanesPerRow * q] = u32x4{};
     if (t == 0) P.lse[orow] = -INFINITY;
     return;
   }
-  // Streaming merge over the pieces, four at a time with every load of a
+  // The lo residue of the row (first-order lse correction, see the decode
+  // epilogue). With one row per wave it is loaded up front, so its latency
+  // passes under the merge; with four, after it (its registers would cost a
+  // wave per SIMD during the merge).
+  u32x4 q8[R];
+  const u32x4* qlo = P.q_lat_lo != nullptr ? reinterpret_cast<const u32x4*>(P.q_lat_lo + orow * kDLat) + t : nullptr;
+  if (R == 1 && qlo != nullptr) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) q8[q] = qlo[kLanesPerRow * q];
+  }
+  // Streaming merge over the pieces, kGroup at a time with every load of a
   // group issued before any is used: running max m, weights exp(lse_k - m).
   float mx = -INFINITY, wsum = 0.f;
-  float o[32];
+  float o[8 * R];
 #pragma unroll
-  for (int v = 0; v < 32; ++v) o[v] = 0.f;
-  for (int k0 = 0; k0 < n; k0 += 4) {
-    float lk[4], sk[4];
-    u32x4 src[4][4];  // 8 fp16 values each
+  for (int v = 0; v < 8 * R; ++v) o[v] = 0.f;
+  for (int k0 = 0; k0 < n; k0 += kGroup) {
+    float lk[kGroup], sk[kGroup];
+    u32x4 src[kGroup][R];  // 8 fp16 values each
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long long prow = (long long)(ns0 + min(k0 + i, n - 1)) * P.M + row;  // short groups repeat the last piece
-      lk[i] = k0 + i < n ? P.part_lse[prow] : -INFINITY;
-      sk[i] = P.part_scale[prow];
-      const u32x4* sp = reinterpret_cast<const u32x4*>(P.part_o + prow * kDLat) + t;
+    for (int i = 0; i < kGroup; ++i) {
+      if (k0 + i < n) {  // uniform: the tail of the last group loads nothing and weighs zero
+        const long long prow = (long long)(ns0 + k0 + i) * P.M + row;
+        lk[i] = P.part_lse[prow];
+        sk[i] = P.part_scale[prow];
+        const u32x4* sp = reinterpret_cast<const u32x4*>(P.part_o + prow * kDLat) + t;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) src[i][q] = sp[16 * q];
+        for (int q = 0; q < R; ++q) src[i][q] = sp[kLanesPerRow * q];
+      } else {
+        lk[i] = -INFINITY;
+        sk[i] = 0.f;
+#pragma unroll
+        for (int q = 0; q < R; ++q) src[i][q] = u32x4{};
+      }
     }
-    const float m_new = fmaxf(fmaxf(mx, fmaxf(lk[0], lk[1])), fmaxf(lk[2], lk[3]));
-    if (m_new == -INFINITY) continue;  // nothing visible yet (uniform over the row's threads)
+    float m_new = mx;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) m_new = fmaxf(m_new, lk[i]);
+    if (m_new == -INFINITY) continue;  // nothing visible yet (uniform over the row's lanes)
     const float alpha = fast_exp2((mx - m_new) * 1.4426950408889634f);  // 0 when mx = -inf
     wsum *= alpha;
 #pragma unroll
-    for (int v = 0; v < 32; ++v) o[v] *= alpha;
+    for (int v = 0; v < 8 * R; ++v) o[v] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w = fast_exp2((lk[i] - m_new) * 1.4426950408889634f);  // 0 for padding entries
+    for (int i = 0; i < kGroup; ++i) {
+      const float w = fast_exp2((lk[i] - m_new) * 1.4426950408889634f);  // 0 for the empty tail
       wsum += w;
       const float ws = w * sk[i];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < R; ++q)
 #pragma unroll
         for (int h2 = 0; h2 < 4; ++h2) {
           const unsigned u = src[i][q][h2];
@@ -939,19 +969,17 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
     mx = m_new;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  float dot = 0.f;  // q_lo . o_lat for the first-order lse correction (see the decode epilogue)
-  const u32x4* qlo = P.q_lat_lo != nullptr ? reinterpret_cast<const u32x4*>(P.q_lat_lo + orow * kDLat) + t : nullptr;
-  u32x4 q8[4];
-  if (qlo != nullptr) {
+  float dot = 0.f;  // q_lo . o_lat
+  if (R != 1 && qlo != nullptr) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) q8[q] = qlo[16 * q];
+    for (int q = 0; q < R; ++q) q8[q] = qlo[kLanesPerRow * q];
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < R; ++q) {
     bf16x8 w;
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = (__bf16)(o[8 * q + e] * inv);
-    out[16 * q] = __builtin_bit_cast(u32x4, w);
+    out[kLanesPerRow * q] = __builtin_bit_cast(u32x4, w);
     if (qlo != nullptr) {
       const bf16x8 qv = __builtin_bit_cast(bf16x8, q8[q]);
 #pragma unroll
@@ -959,7 +987,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
     }
   }
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);  // the row's 16 threads
+  for (int m = kLanesPerRow / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);  // the row's lanes
   if (t == 0)
     P.lse[orow] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 + P.scale * dot : -INFINITY;
 }
@@ -1122,7 +1150,13 @@ extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo,
   }
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: decode launch failed: %s", fn, hipGetErrorString(e));
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(b, (M + 15) / 16), dim3(256), 0, st, P);
+  // The plan cuts the batch into at most b + num_slots - 1 pieces. When that
+  // averages more than four per sequence, one row per combine wave (R = 1);
+  // otherwise four (R = 4).
+  if ((long long)b + num_slots - 1 > 4LL * b)
+    hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(b, (M + 3) / 4), dim3(256), 0, st, P);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<4>, dim3(b, (M + 15) / 16), dim3(256), 0, st, P);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: combine launch failed: %s", fn, hipGetErrorString(e));
   return clear_error();
