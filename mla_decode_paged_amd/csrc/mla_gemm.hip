@@ -53,24 +53,27 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, g = lane >> 5, j16 = lane & 15;
 
+  // stage W[head][:, n0 : n0 + NT]: K rows of NT * 2 bytes. The W loads go
+  // out first and this lane's row of A behind them, so the W tile can be
+  // written to LDS (and the first k-steps multiplied) while A still arrives.
+  constexpr int kRowChunks = NT / 8;
+  constexpr int kPer = K * kRowChunks / 256;
+  u32x4 t[kPer];
+  {
+    const char* wsrc = reinterpret_cast<const char*>(W + (size_t)head * K * N + n0);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + 256 * i, k = c / kRowChunks, ch = c % kRowChunks;
+      t[i] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)k * N * 2 + ch * 16);
+    }
+  }
   // this lane's row of A (padding rows repeat the last row and are never stored)
   const int row = min(r0 + wave * 32 + r32, R - 1);
   const u32x4* arow = reinterpret_cast<const u32x4*>(A + ((size_t)row * h + head) * K) + g;
   bf16x8 af[kKS];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) af[ks] = as_bf16x8(arow[2 * ks]);
-
-  // stage W[head][:, n0 : n0 + NT]: K rows of NT * 2 bytes, all loads first
   {
-    constexpr int kRowChunks = NT / 8;
-    constexpr int kPer = K * kRowChunks / 256;
-    const char* wsrc = reinterpret_cast<const char*>(W + (size_t)head * K * N + n0);
-    u32x4 t[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = threadIdx.x + 256 * i, k = c / kRowChunks, ch = c % kRowChunks;
-      t[i] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)k * N * 2 + ch * 16);
-    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = threadIdx.x + 256 * i, k = c / kRowChunks, ch = c % kRowChunks;
