@@ -51,6 +51,27 @@ def algorithmic_work(inp):
     return dict(kv_bytes=kv_bytes, bytes=kv_bytes + q_bytes + out_bytes + int_bytes, flops=flops)
 
 
+def roofline_bound(work) -> str:
+    """The roofline that bounds the decode call: the bf16 matrix peak when its algorithmic flops per
+    algorithmic byte exceed the chip's balance point (2.5 PF/s over 8 TB/s, about 312 flop/B), else HBM."""
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "mfma" if work["flops"] / work["bytes"] > ridge else "hbm"
+
+
+def roofline_entry(work, t_dec: float, traffic):
+    """roofline object of the JSON line for a decode call of t_dec seconds."""
+    bound = roofline_bound(work)
+    if bound == "mfma":
+        achieved, peak, unit = work["flops"] / t_dec / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work["bytes"] / t_dec / 1e9, HBM_PEAK_GBS, "GB/s"
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "traffic_unit": "HBM bytes per call (calibrated counters)",
+            "kernel": "mla_decode_paged call (split kernel + combine)",
+            "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"]}
+
+
 TRAFFIC_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_metadata.hip")
 
 
@@ -271,11 +292,7 @@ def main():
         "decode_TFLOPs": round(tflops, 2),
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.config),
-                     "traffic_unit": "HBM bytes per call (calibrated counters)",
-                     "kernel": "mla_decode_paged call (split kernel + combine)",
-                     "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"]},
+        "roofline": roofline_entry(work, t_dec, recorded_traffic(args.config)),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

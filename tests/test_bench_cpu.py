@@ -29,3 +29,28 @@ def test_traffic_record_matches_the_kernel_sources(config):
 
 def test_traffic_record_absent_for_unprofiled_workload():
     assert bench.recorded_traffic("no_such_workload") is None
+
+
+def _work(b, s_q, h, seqlens, causal):
+    import types
+
+    import numpy as np
+    inp = types.SimpleNamespace(b=b, s_q=s_q, h=h, causal=causal, seqlens=np.asarray(seqlens, dtype=np.int32))
+    return bench.algorithmic_work(inp)
+
+
+@pytest.mark.parametrize("b,s_q,h,L,causal,bound", [
+    (128, 1, 32, 512, False, "hbm"),     # one tensor-parallel share of the heads
+    (128, 1, 128, 2176, False, "hbm"),   # all heads, the mean length of the uniform 256..4096 draw
+    (128, 2, 128, 4096, True, "mfma"),   # two causal query tokens
+    (32, 8, 128, 2280, True, "mfma"),    # eight-token speculative verify
+])
+def test_roofline_bound_follows_arithmetic_intensity(b, s_q, h, L, causal, bound):
+    """The decode call is priced against HBM below the chip's balance point (2.5 PF/s / 8 TB/s, about
+    312 flop per byte) and against the bf16 matrix peak above it; achieved/peak/unit follow the bound."""
+    work = _work(b, s_q, h, [L] * b, causal)
+    assert bench.roofline_bound(work) == bound
+    r = bench.roofline_entry(work, 1e-4, None)
+    assert r["bound"] == bound and r["unit"] == ("TFLOP/s" if bound == "mfma" else "GB/s")
+    expect = work["flops"] / 1e-4 / 1e12 if bound == "mfma" else work["bytes"] / 1e-4 / 1e9
+    assert abs(r["achieved"] - expect) <= 0.05 and abs(r["frac"] - expect / r["peak"]) <= 1e-4
