@@ -58,6 +58,19 @@ def test_forced_split_counts(gpu_lib, slots):
     res, _ = _check_all(gpu_lib, inp, slots=slots)
 
 
+@pytest.mark.parametrize("b", [84, 86])
+def test_combine_layout_switch(gpu_lib, b):
+    """With 256 slots the plan cuts b sequences into at most b + 255 pieces: 84 sequences average
+    more than four (the combine merges one row per wave) and 86 do not (four rows per wave). Both
+    sides of the switch, with empty and poisoned sequences, every element against the oracle."""
+    rng = np.random.default_rng(30 + b)
+    seqlens = rng.integers(1, 200, b)
+    seqlens[[3, b - 1]] = 0
+    inp = make_inputs("tiny", seed=30 + b, seqlens=seqlens.tolist(), h=16, trap=True)
+    say("combine layout switch: b", b, "slots 256")
+    _check_all(gpu_lib, inp, slots=256)
+
+
 def test_without_lo_plane_long_rows(gpu_lib):
     """On long caches with spread-out attention bf16 q_lat alone meets the bar."""
     inp = make_inputs("full_heads", seed=8, seqlens=[1100, 2500, 4096, 3000])
