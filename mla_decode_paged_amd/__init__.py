@@ -25,7 +25,7 @@ import torch
 
 __all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "decode_paged",
            "up_v", "gather_pages", "append_kv", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
-           "SPLIT_OVERHEAD_FEW_ROWS", "default_split_overhead",
+           "SPLIT_OVERHEAD_FEW_ROWS", "SPLIT_OVERHEAD_ROW_BLOCKS", "default_split_overhead",
            "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE", "MLA_DEVERR_PAGE_ID",
            "MLA_DEVERR_SEQ_TOO_LONG", "MLA_DEVERR_SHORT_SEQ"]
 
@@ -44,6 +44,10 @@ SPLIT_OVERHEAD = 6
 # much and whose pieces start in a shared burst of first-tile loads; a sweep
 # of 0..16 on the 32-head workload spans 30.1-33.1 us, 30.7 at 2):
 SPLIT_OVERHEAD_FEW_ROWS = 2
+# More than 128 rows (several row blocks per slot, speculative verify with
+# 8 query tokens at 128 heads: F = 2/4/6/10/16 give 202.8/195.0/200.7/213.0/
+# 231.4 us per call; 2 causal tokens with equal lengths do not split):
+SPLIT_OVERHEAD_ROW_BLOCKS = 4
 
 _lib = None
 _P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -127,7 +131,10 @@ def workspace_bytes(b: int, s_q: int, h: int, slots: int) -> int:
 
 
 def default_split_overhead(s_q: int, h: int) -> int:
-    return SPLIT_OVERHEAD_FEW_ROWS if s_q * h <= 32 else SPLIT_OVERHEAD
+    m = s_q * h
+    if m <= 32:
+        return SPLIT_OVERHEAD_FEW_ROWS
+    return SPLIT_OVERHEAD if m <= 128 else SPLIT_OVERHEAD_ROW_BLOCKS
 
 
 def get_metadata(cache_seqlens: torch.Tensor, slots: int | None = None, s_q: int = 1, h: int = 128,
