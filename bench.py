@@ -1,7 +1,9 @@
 """Benchmark: one decode step of the paged MLA hot path on one MI355X.
 
-A step is the whole path on one batch: mla_get_metadata, mla_absorb_q,
-mla_decode_paged (split kernel + combine) and mla_up_v. The cache append
+A step is the whole path on one batch: the split plan and the query
+absorption (one launch, mla_absorb_q_with_plan; --separate-plan runs
+mla_get_metadata and mla_absorb_q instead), mla_decode_paged (split kernel +
+combine) and mla_up_v. The cache append
 (mla_append_kv) is timed on its own after the steps and reported beside them. Inputs are seeded
 synthetic tensors already resident in HBM. To keep the 256 MB Infinity Cache
 from serving repeats, R copies of every input and output rotate, with R times
@@ -72,7 +74,7 @@ def roofline_entry(work, t_dec: float, traffic):
             "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"]}
 
 
-TRAFFIC_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_metadata.hip")
+TRAFFIC_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_metadata.hip", "mla_plan.h")
 
 
 def recorded_traffic(config: str):
@@ -158,6 +160,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-plan", action="store_true",
+                    help="plan with mla_get_metadata and absorb with mla_absorb_q (two launches) instead of "
+                         "mla_absorb_q_with_plan")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the steps as eager launches only (value = eager wall time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -206,17 +211,24 @@ def main():
         s["ns"] = torch.empty((inp.b + 1,), dtype=torch.int32, device="cuda")
     ws = torch.empty((mla.workspace_bytes(inp.b, inp.s_q, inp.h, slots),), dtype=torch.uint8, device="cuda")
 
-    ev = {k: [] for k in ("meta", "absorb", "decode", "up_v")}
+    first = ("meta", "absorb") if args.separate_plan else ("plan_absorb",)
+    ev = {k: [] for k in first + ("decode", "up_v")}
 
     def step(i, timed):
         s = sets[i % R]
         e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
         if timed:
             e[0].record()
-        meta, ns = mla.get_metadata(s["sl"], slots, s_q=inp.s_q, h=inp.h, out=(s["meta"], s["ns"]))
-        if timed:
-            e[1].record()
-        mla.absorb_q(s["q_nope"], s["w_uk"], out=(s["q_lat"], s["q_lo"]))
+        if args.separate_plan:
+            meta, ns = mla.get_metadata(s["sl"], slots, s_q=inp.s_q, h=inp.h, out=(s["meta"], s["ns"]))
+            if timed:
+                e[1].record()
+            mla.absorb_q(s["q_nope"], s["w_uk"], out=(s["q_lat"], s["q_lo"]))
+        else:
+            _, (meta, ns) = mla.absorb_q_with_plan(s["q_nope"], s["w_uk"], s["sl"],
+                                                   out=((s["q_lat"], s["q_lo"]), (s["meta"], s["ns"])))
+            if timed:
+                e[1].record()
         if timed:
             e[2].record()
         mla.decode_paged(s["q_lat"], s["q_pe"], s["kv"], s["bt"], s["sl"], meta, ns, inp.scale, inp.causal,
@@ -226,7 +238,8 @@ def main():
         mla.up_v(s["o_lat"], s["w_uv"], out=s["o"])
         if timed:
             e[4].record()
-            for k, a, b in (("meta", 0, 1), ("absorb", 1, 2), ("decode", 2, 3), ("up_v", 3, 4)):
+            stages = ((("meta", 0, 1), ("absorb", 1, 2)) if args.separate_plan else (("plan_absorb", 0, 1),))
+            for k, a, b in stages + (("decode", 2, 3), ("up_v", 3, 4)):
                 ev[k].append((e[a], e[b]))
 
     for i in range(args.warmup):

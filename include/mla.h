@@ -117,6 +117,24 @@ int mla_get_metadata(const int32_t* cache_seqlens, int b, int num_slots, int spl
 int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_lat, uint16_t* q_lat_lo,
                  int b, int s_q, int h, void* stream);
 
+/* mla_absorb_q_with_plan - mla_get_metadata and mla_absorb_q in one launch.
+ * The plan reads only cache_seqlens and the absorption only the queries and
+ * W_UK, so one workgroup plans while the others multiply; the launch that
+ * would run the plan alone is saved. That pays only while every workgroup of
+ * the GEMM is resident at once: when its tiles already fill the CUs (128
+ * heads at b = 128, or more rows), the call runs the two kernels back to back
+ * instead. Meant for the first layer of a decode step; later layers reuse
+ * the plan and call mla_absorb_q.
+ *
+ * Arguments, outputs and error behaviour are those of the two calls:
+ * q_nope, w_uk, q_lat, q_lat_lo, b, s_q, h as for mla_absorb_q;
+ * cache_seqlens, num_slots, split_overhead, tile_meta, num_splits as for
+ * mla_get_metadata (b <= MLA_MAX_BATCH). Both outputs are bit-identical to
+ * those of the separate calls. Every check runs before the launch. */
+int mla_absorb_q_with_plan(const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_lat, uint16_t* q_lat_lo,
+                           int b, int s_q, int h, const int32_t* cache_seqlens, int num_slots, int split_overhead,
+                           int32_t* tile_meta, int32_t* num_splits, void* stream);
+
 /* mla_decode_paged - paged MLA decode in the absorbed form.
  *
  * For sequence b and row r = (j, i) the kernel scores every visible cached

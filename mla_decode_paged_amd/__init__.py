@@ -23,7 +23,8 @@ import os
 
 import torch
 
-__all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "decode_paged",
+__all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "absorb_q_with_plan",
+           "decode_paged",
            "up_v", "gather_pages", "append_kv", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
            "SPLIT_OVERHEAD_FEW_ROWS", "SPLIT_OVERHEAD_ROW_BLOCKS", "default_split_overhead",
            "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE", "MLA_DEVERR_PAGE_ID",
@@ -71,6 +72,7 @@ def load():
         "mla_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
         "mla_get_metadata": (_I, [_P, _I, _I, _I, _P, _P, _P]),
         "mla_absorb_q": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
+        "mla_absorb_q_with_plan": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _P]),
         "mla_decode_paged": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
                                   _P, _P, _P]),
         "mla_up_v": (_I, [_P, _P, _P, _I, _I, _I, _P]),
@@ -173,6 +175,37 @@ def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, lo: bool = True, out=None
                                _ptr(q_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)), b, s_q, h, _stream()),
            "mla_absorb_q")
     return q_lat, q_lo
+
+
+def absorb_q_with_plan(q_nope: torch.Tensor, w_uk: torch.Tensor, cache_seqlens: torch.Tensor,
+                       slots: int | None = None, split_overhead: int | None = None, lo: bool = True, out=None):
+    """get_metadata and absorb_q in one launch (the first layer of a step):
+    ((q_lat, q_lat_lo), (tile_meta, num_splits)). ``out`` is ((q_lat, q_lo), (tile_meta, num_splits))."""
+    b, s_q, h, dn = q_nope.shape
+    dev = q_nope.device
+    if cache_seqlens.numel() != b:
+        raise MLAError(f"cache_seqlens has {cache_seqlens.numel()} entries, expected {b}")
+    if split_overhead is None:
+        split_overhead = default_split_overhead(s_q, h)
+    if out is None:
+        if slots is None:
+            slots = num_slots(b, s_q, h)
+        q_lat = torch.empty((b, s_q, h, D_LATENT), dtype=torch.bfloat16, device=dev)
+        q_lo = torch.empty_like(q_lat) if lo else None
+        tile_meta = torch.empty((slots, META_WORDS), dtype=torch.int32, device=dev)
+        num_splits = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    else:
+        (q_lat, q_lo), (tile_meta, num_splits) = out
+        slots = tile_meta.shape[0]
+    _check(load().mla_absorb_q_with_plan(_ptr(q_nope, "q_nope", _BF16, (b, s_q, h, D_NOPE)),
+                                         _ptr(w_uk, "w_uk", _BF16, (h, D_NOPE, D_LATENT)),
+                                         _ptr(q_lat, "q_lat", _BF16, (b, s_q, h, D_LATENT)),
+                                         _ptr(q_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)), b, s_q, h,
+                                         _ptr(cache_seqlens, "cache_seqlens", _I32), slots, split_overhead,
+                                         _ptr(tile_meta, "tile_meta", _I32, (slots, META_WORDS)),
+                                         _ptr(num_splits, "num_splits", _I32, (b + 1,)), _stream()),
+           "mla_absorb_q_with_plan")
+    return (q_lat, q_lo), (tile_meta, num_splits)
 
 
 def decode_paged(q_lat, q_pe, kv_cache, block_table, cache_seqlens, tile_meta, num_splits, softmax_scale,

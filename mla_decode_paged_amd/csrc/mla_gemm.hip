@@ -21,8 +21,11 @@
 // writes and leaves as whole row segments (NT * 2 contiguous bytes per row).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "mla_device.h"
 #include "mla_host.h"
+#include "mla_plan.h"
 
 namespace mla {
 
@@ -30,24 +33,29 @@ constexpr int kGemmRows = 128;  // rows per workgroup: 4 waves x 32
 constexpr int kBufferWord3G = 0x00020000;  // raw buffer resource: dword data, bounds-checked
 constexpr int kStoreNT = 2;                 // buffer store cache policy: non-temporal
 
+// LDS bytes of one tile (the staged W tile, then the output planes).
 template <int K, int N, int NT>
-__global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                                        uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
-                                                        int R, int h) {
+constexpr int gemm_smem_bytes() {
+  constexpr int kWBytes = K * (NT * 2 + 16);
+  constexpr int kOBytes = kGemmRows * (NT * 2 + 16);
+  return kWBytes > 2 * kOBytes ? kWBytes : 2 * kOBytes;
+}
+
+// One output tile of the per-head GEMM, by the workgroup with id `bid`.
+template <int K, int N, int NT>
+__device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                               uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo, int R,
+                                               int h, int bid, MLA_LDS char* lds) {
   constexpr int kWPitch = NT * 2 + 16;          // bytes per staged W row (k)
   constexpr int kOPitch = NT * 2 + 16;          // bytes per staged output row
-  constexpr int kWBytes = K * kWPitch;
   constexpr int kOBytes = kGemmRows * kOPitch;  // one output plane (hi or lo)
-  constexpr int kSmem = kWBytes > 2 * kOBytes ? kWBytes : 2 * kOBytes;
   constexpr int kNT = NT / 32;                  // 32-column MFMA tiles per wave
   constexpr int kKS = K / 16;                   // k-steps
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  MLA_LDS char* lds = (MLA_LDS char*)(smem);
   // workgroup -> (head, row block, column tile): head = 8 j + (id % 8) for
   // the j-th run of tiles on XCD id % 8
   constexpr int kTilesN = N / NT;
   const int per_head = kTilesN * ((R + kGemmRows - 1) / kGemmRows);
-  const int idx = blockIdx.x >> 3, head = (idx / per_head) * 8 + (blockIdx.x & 7), inner = idx % per_head;
+  const int idx = bid >> 3, head = (idx / per_head) * 8 + (bid & 7), inner = idx % per_head;
   if (head >= h) return;
   const int n0 = (inner % kTilesN) * NT, r0 = (inner / kTilesN) * kGemmRows;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -144,6 +152,39 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
   }
 }
 
+template <int K, int N, int NT>
+__global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                                        uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
+                                                        int R, int h) {
+  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<K, N, NT>()];
+  head_gemm_tile<K, N, NT>(A, W, out, out_lo, R, h, blockIdx.x, (MLA_LDS char*)(smem));
+}
+
+// The split-KV plan and the query absorption in one launch: the plan reads
+// only the cache lengths and the absorption only the queries, so workgroup 0
+// plans (mla_plan.h, 256 threads) while the others run the GEMM tiles.
+// Workgroups 1..7 have no work; the tiles start at id 8, so that id % 8 is
+// still the XCD of a tile. LDS is dynamic: the larger of a tile's and the
+// plan's (2 (b + 1) + 5 ints).
+constexpr int kPlanWGs = 8;
+
+template <int NT>
+__global__ __launch_bounds__(256) void absorb_plan_kernel(const uint16_t* __restrict__ A,
+                                                          const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
+                                                          uint16_t* __restrict__ out_lo, int R, int h,
+                                                          const int32_t* seqlens, int b, int n_slots, int F,
+                                                          int32_t* meta, int32_t* ns_out) {
+  extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+  if (blockIdx.x < kPlanWGs) {
+    if (blockIdx.x == 0) {
+      int* C = reinterpret_cast<int*>(dyn_smem);
+      plan_block<256>(seqlens, b, n_slots, F, meta, ns_out, C, C + (b + 1), C + 2 * (b + 1));
+    }
+    return;
+  }
+  head_gemm_tile<kDNope, kDLat, NT>(A, W, out, out_lo, R, h, blockIdx.x - kPlanWGs, (MLA_LDS char*)(dyn_smem));
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -180,6 +221,52 @@ extern "C" int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return clear_error();
+}
+
+extern "C" int mla_absorb_q_with_plan(const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_lat,
+                                      uint16_t* q_lat_lo, int b, int s_q, int h, const int32_t* cache_seqlens,
+                                      int num_slots, int split_overhead, int32_t* tile_meta, int32_t* num_splits,
+                                      void* stream) {
+  const char* fn = "mla_absorb_q_with_plan";
+  if (int rc = check_ptr16(fn, q_nope, "q_nope")) return rc;
+  if (int rc = check_ptr16(fn, w_uk, "w_uk")) return rc;
+  if (int rc = check_ptr16(fn, q_lat, "q_lat")) return rc;
+  if (q_lat_lo && reinterpret_cast<uintptr_t>(q_lat_lo) % 16)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: q_lat_lo must be 16-byte aligned", fn);
+  if (int rc = check_shape(fn, b, s_q, h)) return rc;
+  if (int rc = check_plan_args(fn, cache_seqlens, b, num_slots, split_overhead, tile_meta, num_splits)) return rc;
+  const int R = b * s_q;
+  const int rb = (R + kGemmRows - 1) / kGemmRows;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int hg = (h + 7) / 8 * 8;
+  const size_t plan_bytes = sizeof(int) * (2 * ((size_t)b + 1) + 256 / 64 + 1);
+  // tile widths as in mla_absorb_q
+  const int nt = h <= 32 ? 64 : 128;
+  const int tiles = kDLat / nt * rb * hg;
+  const size_t smem = std::max(plan_bytes, (size_t)(nt == 64 ? gemm_smem_bytes<kDNope, kDLat, 64>()
+                                                             : gemm_smem_bytes<kDNope, kDLat, 128>()));
+  // One launch pays only while every workgroup is resident at once: when the
+  // tiles already fill each CU's LDS, the plan's workgroups would push tiles
+  // into a second round, so the plan then runs as its own launch ahead of
+  // the GEMM (same results).
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return set_error(MLA_ERR_HIP, "%s: cannot query the device", fn);
+  const long long resident = (long long)cus * std::min<long long>(8, (160 * 1024) / (long long)smem);
+  if (tiles + kPlanWGs <= resident) {
+    if (nt == 64)
+      hipLaunchKernelGGL(absorb_plan_kernel<64>, dim3(kPlanWGs + tiles), dim3(256), smem, st, q_nope, w_uk, q_lat,
+                         q_lat_lo, R, h, cache_seqlens, b, num_slots, split_overhead, tile_meta, num_splits);
+    else
+      hipLaunchKernelGGL(absorb_plan_kernel<128>, dim3(kPlanWGs + tiles), dim3(256), smem, st, q_nope, w_uk,
+                         q_lat, q_lat_lo, R, h, cache_seqlens, b, num_slots, split_overhead, tile_meta, num_splits);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess)
+      return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return clear_error();
+  }
+  if (int rc = mla_get_metadata(cache_seqlens, b, num_slots, split_overhead, tile_meta, num_splits, stream)) return rc;
+  return mla_absorb_q(q_nope, w_uk, q_lat, q_lat_lo, b, s_q, h, stream);
 }
 
 extern "C" int mla_up_v(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int b, int s_q, int h,

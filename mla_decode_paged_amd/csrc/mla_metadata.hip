@@ -1,131 +1,21 @@
-// Split-KV work plan (mla_get_metadata).
-//
-// FlashMLA's usage plans the tile schedule and split counts once per decode
-// step from the cache lengths and reuses them for every layer (FlashMLA
-// release news, usage example); the SC11 note likewise picks how to spread
-// one decode over its cores by batch count and sequence length. This plan is
-// the library's own: sequences with pages are laid end to end on a cost line,
-// F + pages units each (F = split_overhead), and slot s takes the units
-// [s q, (s+1) q) with q = ceil(total / num_slots). Every page lands in exactly
-// one slot; the pages of one sequence inside one slot form a piece (a split).
-//
-// One workgroup of 1024 threads: block scans give each sequence's start on the
-// cost line and its split prefix, then every slot finds its first and last
-// sequence by binary search. All integer; the result is bit-identical to the
-// interval definition above.
+// mla_get_metadata: the split-KV work plan (mla_plan.h) by one workgroup of
+// 1024 threads.
 #include <hip/hip_runtime.h>
 
 #include "mla_device.h"
 #include "mla_host.h"
+#include "mla_plan.h"
 
 namespace mla {
 
 constexpr int kPlanThreads = 1024;
 
-__device__ __forceinline__ int pages_of(int L) { return L > 0 ? (L + kPage - 1) / kPage : 0; }
-
-// Exclusive prefix sum over the workgroup; also returns the total.
-__device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) wave_sums[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      const int x = wave_sums[w];
-      wave_sums[w] = run;
-      run += x;
-    }
-    wave_sums[kPlanThreads / 64] = run;
-  }
-  __syncthreads();
-  const int excl = incl - v + wave_sums[wave];
-  *total = wave_sums[kPlanThreads / 64];
-  __syncthreads();  // wave_sums is reused by the next scan
-  return excl;
-}
-
 __global__ __launch_bounds__(kPlanThreads) void mla_metadata_kernel(const int32_t* seqlens, int b, int n_slots,
                                                                     int F, int32_t* meta, int32_t* ns_out) {
   __shared__ int C[MLA_MAX_BATCH + 1];   // cost-line start of each sequence; C[b] = total
   __shared__ int NS[MLA_MAX_BATCH + 1];  // split prefix
-  __shared__ int PG[MLA_MAX_BATCH];      // pages per sequence
   __shared__ int wave_sums[kPlanThreads / 64 + 1];
-  const int tid = threadIdx.x;
-  const int per = (b + kPlanThreads - 1) / kPlanThreads;
-  const int lo = min(tid * per, b), hi = min(lo + per, b);
-
-  int local = 0;
-  for (int i = lo; i < hi; ++i) {
-    const int pg = pages_of(seqlens[i]);
-    PG[i] = pg;
-    local += pg > 0 ? F + pg : 0;
-  }
-  int T;
-  int run = block_exclusive_scan(local, wave_sums, &T);
-  for (int i = lo; i < hi; ++i) {
-    C[i] = run;
-    run += PG[i] > 0 ? F + PG[i] : 0;
-  }
-  if (tid == 0) C[b] = T;
-  const int q = T > 0 ? max(1, (T + n_slots - 1) / n_slots) : 1;
-
-  int nsplit = 0;
-  for (int i = lo; i < hi; ++i)
-    if (PG[i] > 0) nsplit += (C[i] + F + PG[i] - 1) / q - (C[i] + F) / q + 1;
-  int total_splits;
-  run = block_exclusive_scan(nsplit, wave_sums, &total_splits);
-  for (int i = lo; i < hi; ++i) {
-    NS[i] = run;
-    if (PG[i] > 0) run += (C[i] + F + PG[i] - 1) / q - (C[i] + F) / q + 1;
-  }
-  if (tid == 0) NS[b] = total_splits;
-  __syncthreads();
-
-  for (int i = tid; i <= b; i += kPlanThreads) ns_out[i] = NS[i];
-
-  for (int s = tid; s < n_slots; s += kPlanThreads) {
-    int* m = meta + (long long)s * MLA_META_WORDS;
-    const long long lo_u = (long long)s * q;
-    const long long hi_u = min((long long)(s + 1) * q, (long long)T);
-    int bf = 0, bl = -1;
-    if (lo_u < T) {
-      // first sequence whose cost interval ends past lo_u
-      int a = 0, e = b;  // search in [a, e)
-      while (a < e) {
-        const int mid = (a + e) >> 1;
-        if (C[mid + 1] > lo_u) e = mid; else a = mid + 1;
-      }
-      bf = a;
-      if (C[bf] + F < hi_u) {
-        // last sequence whose pages start before hi_u
-        a = 0;
-        e = b;
-        while (a < e) {
-          const int mid = (a + e) >> 1;
-          if (C[mid] + F < hi_u) a = mid + 1; else e = mid;
-        }
-        bl = a - 1;
-      }
-    }
-    if (bl < bf) {
-      m[0] = 0; m[1] = 0; m[2] = -1; m[3] = 0; m[4] = 0;
-    } else {
-      const long long sb = C[bf] + F, sl = C[bl] + F;
-      m[0] = bf;
-      m[1] = (int)(max(lo_u, sb) - sb);
-      m[2] = bl;
-      m[3] = (int)(min(hi_u, (long long)C[bl + 1]) - sl);
-      m[4] = NS[bf] + (s - (int)(sb / q));
-    }
-    m[5] = 0; m[6] = 0; m[7] = 0;
-  }
+  plan_block<kPlanThreads>(seqlens, b, n_slots, F, meta, ns_out, C, NS, wave_sums);
 }
 
 }  // namespace mla
@@ -133,12 +23,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_metadata_kernel(const int32_
 extern "C" int mla_get_metadata(const int32_t* cache_seqlens, int b, int num_slots, int split_overhead,
                                 int32_t* tile_meta, int32_t* num_splits, void* stream) {
   const char* fn = "mla_get_metadata";
-  if (!cache_seqlens || !tile_meta || !num_splits)
-    return mla::set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
-  if (b < 1 || b > MLA_MAX_BATCH)
-    return mla::set_error(MLA_ERR_INVALID_ARG, "%s: b must be in [1, %d] (got %d)", fn, MLA_MAX_BATCH, b);
-  if (num_slots < 1) return mla::set_error(MLA_ERR_INVALID_ARG, "%s: num_slots must be >= 1", fn);
-  if (split_overhead < 0) return mla::set_error(MLA_ERR_INVALID_ARG, "%s: split_overhead must be >= 0", fn);
+  if (int rc = mla::check_plan_args(fn, cache_seqlens, b, num_slots, split_overhead, tile_meta, num_splits))
+    return rc;
   hipLaunchKernelGGL(mla::mla_metadata_kernel, dim3(1), dim3(mla::kPlanThreads), 0,
                      static_cast<hipStream_t>(stream), cache_seqlens, b, num_slots, split_overhead, tile_meta,
                      num_splits);

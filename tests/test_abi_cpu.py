@@ -110,3 +110,28 @@ def test_other_calls_reject(lib):
     assert lib.mla_num_slots(2, 1, 16, None) == INVALID
     assert lib.mla_take_device_error(None) == INVALID
     assert lib.mla_last_error().decode() != ""
+
+
+def _absorb_plan(lib, **kw):
+    a = dict(q_nope=FAKE, w_uk=FAKE, q_lat=FAKE, q_lo=None, b=2, s_q=1, h=16, sl=FAKE, slots=8, F=2, meta=FAKE,
+             ns=FAKE)
+    a.update(kw)
+    return lib.mla_absorb_q_with_plan(a["q_nope"], a["w_uk"], a["q_lat"], a["q_lo"], a["b"], a["s_q"], a["h"],
+                                      a["sl"], a["slots"], a["F"], a["meta"], a["ns"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q_nope=None), INVALID, "q_nope"),
+    (dict(q_lo=ctypes.c_void_p((1 << 20) + 8)), INVALID, "aligned"),
+    (dict(h=100), UNSUPPORTED, "h must be"),
+    (dict(s_q=0), INVALID, "s_q"),
+    (dict(sl=None), INVALID, "NULL"),
+    (dict(meta=None), INVALID, "NULL"),
+    (dict(b=9000), INVALID, "b must be"),
+    (dict(slots=0), INVALID, "num_slots"),
+    (dict(F=-1), INVALID, "split_overhead"),
+])
+def test_absorb_with_plan_rejects(lib, kw, code, msg):
+    """The combined call applies the checks of both calls before anything is launched."""
+    assert _absorb_plan(lib, **kw) == code
+    assert msg in lib.mla_last_error().decode()

@@ -91,3 +91,29 @@ def test_plan_into_given_buffers(gpu_lib):
     for out in bad:
         with pytest.raises(mla.MLAError):
             mla.get_metadata(sl, slots, split_overhead=2, out=out)
+
+
+@pytest.mark.parametrize("b,s_q,h,slots,F", [
+    (2, 1, 16, 4, 2), (128, 1, 128, 256, 6), (128, 1, 32, 256, 2), (32, 8, 128, 32, 4),
+    (300, 2, 64, 97, 3), (8192, 1, 16, 1000, 4),
+])
+def test_absorb_with_plan_matches_separate_calls(gpu_lib, b, s_q, h, slots, F):
+    """mla_absorb_q_with_plan gives bit for bit the q_lat, q_lat_lo, tile_meta and num_splits of
+    mla_absorb_q and mla_get_metadata (the plan by a 256-thread workgroup inside the GEMM launch)."""
+    mla = gpu_lib
+    rng = np.random.default_rng(40 + b)
+    seqlens = rng.integers(0, 5000, b).astype(np.int32)
+    seqlens[0] = 0
+    say("absorb+plan b", b, "s_q", s_q, "h", h, "slots", slots, "F", F)
+    sl = torch.tensor(seqlens, device="cuda")
+    q_nope = torch.from_numpy(rng.standard_normal((b, s_q, h, 128)).astype(np.float32)).to(torch.bfloat16).cuda()
+    w_uk = torch.from_numpy((rng.standard_normal((h, 128, 512)) / np.sqrt(512)).astype(np.float32)).to(torch.bfloat16).cuda()
+    (ql, qlo), (meta, ns) = mla.absorb_q_with_plan(q_nope, w_uk, sl, slots, split_overhead=F)
+    ql2, qlo2 = mla.absorb_q(q_nope, w_uk)
+    meta2, ns2 = mla.get_metadata(sl, slots, split_overhead=F)
+    torch.cuda.synchronize()
+    assert torch.equal(ql.view(torch.int16), ql2.view(torch.int16))
+    assert torch.equal(qlo.view(torch.int16), qlo2.view(torch.int16))
+    assert torch.equal(meta, meta2) and torch.equal(ns, ns2)
+    ref_meta, ref_ns, _ = SP.plan(seqlens.tolist(), slots, F)
+    assert np.array_equal(meta.cpu().numpy(), ref_meta) and np.array_equal(ns.cpu().numpy(), ref_ns)
