@@ -33,12 +33,12 @@ constexpr int kGemmRows = 128;  // rows per workgroup: 4 waves x 32
 constexpr int kBufferWord3G = 0x00020000;  // raw buffer resource: dword data, bounds-checked
 constexpr int kStoreNT = 2;                 // buffer store cache policy: non-temporal
 
-// LDS bytes of one tile (the staged W tile, then the output planes).
+// LDS bytes of one tile (the staged W tile, then one output plane at a time).
 template <int K, int N, int NT>
 constexpr int gemm_smem_bytes() {
   constexpr int kWBytes = K * (NT * 2 + 16);
   constexpr int kOBytes = kGemmRows * (NT * 2 + 16);
-  return kWBytes > 2 * kOBytes ? kWBytes : 2 * kOBytes;
+  return kWBytes > kOBytes ? kWBytes : kOBytes;
 }
 
 // One output tile of the per-head GEMM, by the workgroup with id `bid`.
@@ -107,53 +107,58 @@ __device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, c
   __syncthreads();  // every wave is done reading the W tile
 
   // lane holds C^T[column 32 t + 8 q + 4 g + e][row r32], e = 0..3, in c[t][4 q + e]
+  // Each wave stages its own 32 rows in LDS and stores them as row segments
+  // (only its own LDS rows are read back), first the bf16 values, then in
+  // the same rows their rounding residues: a wave's LDS operations complete
+  // in order, so the residue writes follow the reads of the values, and one
+  // plane of LDS suffices. The stores are non-temporal (cache policy nt):
+  // the outputs stream out, and nothing in this kernel reads them back.
   const int orow = wave * 32 + r32;
-#pragma unroll
-  for (int t = 0; t < kNT; ++t)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x4 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = c[t][4 * q + e];
-        hi[e] = (__bf16)v;
-        lo[e] = (__bf16)(v - (float)hi[e]);
-      }
-      const int off = orow * kOPitch + (32 * t + 8 * q + 4 * g) * 2;
-      *reinterpret_cast<MLA_LDS bf16x4*>(lds + off) = hi;
-      if (out_lo != nullptr) *reinterpret_cast<MLA_LDS bf16x4*>(lds + kOBytes + off) = lo;
-    }
-  // each wave stores its own 32 rows (only its own LDS rows are read back);
-  // the stores are non-temporal (cache policy nt): the outputs stream out,
-  // and nothing in this kernel reads them back
   constexpr int kLanesPerRow = NT * 2 / 16;
   constexpr int kRowsPerInstr = 64 / kLanesPerRow;
   const int rr = lane / kLanesPerRow, ch = lane % kLanesPerRow;
   const size_t row_stride = (size_t)h * N * 2;  // bytes between consecutive rows of one head
   const int valid = min(kGemmRows, R - r0);
   const unsigned nbytes = (unsigned)((size_t)(valid - 1) * row_stride + NT * 2);
-  uint16_t* obase = out + ((size_t)r0 * h + head) * N + n0;
-  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, nbytes, kBufferWord3G);
+  // the values go to LDS as they are rounded; their residues wait in
+  // registers (32 per lane) until the values have left
+  bf16x4 vlo[kNT * 4];
 #pragma unroll
-  for (int k = 0; k < 32; k += kRowsPerInstr) {
-    const int lr = wave * 32 + k + rr;
-    const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(lds + lr * kOPitch + ch * 16);
-    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (unsigned)(lr * row_stride) + ch * 16, 0, kStoreNT);
-  }
-  if (out_lo != nullptr) {
-    const __amdgpu_buffer_rsrc_t rlo = __builtin_amdgcn_make_buffer_rsrc(
-        out_lo + ((size_t)r0 * h + head) * N + n0, 0, nbytes, kBufferWord3G);
+  for (int t = 0; t < kNT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = c[t][4 * q + e];
+        hi[e] = (__bf16)v;
+        vlo[4 * t + q][e] = (__bf16)(v - (float)hi[e]);
+      }
+      *reinterpret_cast<MLA_LDS bf16x4*>(lds + orow * kOPitch + (32 * t + 8 * q + 4 * g) * 2) = hi;
+    }
+  auto store_rows = [&](uint16_t* dst) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(dst + ((size_t)r0 * h + head) * N + n0, 0,
+                                                                        nbytes, kBufferWord3G);
 #pragma unroll
     for (int k = 0; k < 32; k += kRowsPerInstr) {
       const int lr = wave * 32 + k + rr;
-      const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(lds + kOBytes + lr * kOPitch + ch * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(v, rlo, (unsigned)(lr * row_stride) + ch * 16, 0, kStoreNT);
+      const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(lds + lr * kOPitch + ch * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (unsigned)(lr * row_stride) + ch * 16, 0, kStoreNT);
     }
+  };
+  store_rows(out);
+  if (out_lo != nullptr) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<MLA_LDS bf16x4*>(lds + orow * kOPitch + (32 * t + 8 * q + 4 * g) * 2) = vlo[4 * t + q];
+    store_rows(out_lo);
   }
 }
 
 template <int K, int N, int NT>
-__global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(K == kDNope ? 3 : 1))) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                         uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
                                                         int R, int h) {
   __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<K, N, NT>()];
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(const uint16_t* __restri
 constexpr int kPlanWGs = 8;
 
 template <int NT>
-__global__ __launch_bounds__(256) void absorb_plan_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void absorb_plan_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
                                                           uint16_t* __restrict__ out_lo, int R, int h,
                                                           const int32_t* seqlens, int b, int n_slots, int F,
@@ -246,15 +251,17 @@ extern "C" int mla_absorb_q_with_plan(const uint16_t* q_nope, const uint16_t* w_
   const size_t smem = std::max(plan_bytes, (size_t)(nt == 64 ? gemm_smem_bytes<kDNope, kDLat, 64>()
                                                              : gemm_smem_bytes<kDNope, kDLat, 128>()));
   // One launch pays only while every workgroup is resident at once: when the
-  // tiles already fill each CU's LDS, the plan's workgroups would push tiles
-  // into a second round, so the plan then runs as its own launch ahead of
-  // the GEMM (same results).
-  int dev = 0, cus = 0;
+  // tiles already fill the CUs (registers or LDS), the plan's workgroups would
+  // push tiles into a second round, so the plan then runs as its own launch
+  // ahead of the GEMM (same results).
+  int dev = 0, cus = 0, per_cu = 0;
+  const void* fused = nt == 64 ? reinterpret_cast<const void*>(absorb_plan_kernel<64>)
+                               : reinterpret_cast<const void*>(absorb_plan_kernel<128>);
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused, 256, smem) != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: cannot query the device", fn);
-  const long long resident = (long long)cus * std::min<long long>(8, (160 * 1024) / (long long)smem);
-  if (tiles + kPlanWGs <= resident) {
+  if (tiles + kPlanWGs <= (long long)cus * per_cu) {
     if (nt == 64)
       hipLaunchKernelGGL(absorb_plan_kernel<64>, dim3(kPlanWGs + tiles), dim3(256), smem, st, q_nope, w_uk, q_lat,
                          q_lat_lo, R, h, cache_seqlens, b, num_slots, split_overhead, tile_meta, num_splits);
