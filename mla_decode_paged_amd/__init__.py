@@ -211,6 +211,8 @@ def absorb_q_with_plan(q_nope: torch.Tensor, w_uk: torch.Tensor, cache_seqlens: 
 def decode_paged(q_lat, q_pe, kv_cache, block_table, cache_seqlens, tile_meta, num_splits, softmax_scale,
                  causal, q_lat_lo=None, workspace=None, out=None):
     """Paged absorbed-form decode: (o_lat bf16 [b, s_q, h, 512], lse fp32 [b, s_q, h])."""
+    if q_lat.dim() != 4 or tile_meta.dim() != 2:
+        raise MLAError(f"q_lat must be [b, s_q, h, {D_LATENT}] and tile_meta [slots, {META_WORDS}]")
     b, s_q, h, _ = q_lat.shape
     slots = tile_meta.shape[0]
     dev = q_lat.device
@@ -224,12 +226,15 @@ def decode_paged(q_lat, q_pe, kv_cache, block_table, cache_seqlens, tile_meta, n
         o_lat, lse = out
     if kv_cache.dim() != 3 or tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_ROW):
         raise MLAError(f"kv_cache must be [num_pages, {PAGE_TOKENS}, {D_ROW}]")
+    if block_table.dim() != 2:
+        raise MLAError(f"block_table must be [b, max_blocks], got shape {tuple(block_table.shape)}")
     _check(load().mla_decode_paged(
-        _ptr(q_lat, "q_lat", _BF16), _ptr(q_lat_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)),
+        _ptr(q_lat, "q_lat", _BF16, (b, s_q, h, D_LATENT)), _ptr(q_lat_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)),
         _ptr(q_pe, "q_pe", _BF16, (b, s_q, h, D_ROPE)), _ptr(kv_cache, "kv_cache", _BF16), kv_cache.shape[0],
-        _ptr(block_table, "block_table", _I32), block_table.shape[1],
+        _ptr(block_table, "block_table", _I32, (b, block_table.shape[1])), block_table.shape[1],
         _ptr(cache_seqlens, "cache_seqlens", _I32, (b,)), b, s_q, h, float(softmax_scale), int(bool(causal)),
-        _ptr(tile_meta, "tile_meta", _I32), _ptr(num_splits, "num_splits", _I32, (b + 1,)), slots,
+        _ptr(tile_meta, "tile_meta", _I32, (slots, META_WORDS)), _ptr(num_splits, "num_splits", _I32, (b + 1,)),
+        slots,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(o_lat, "o_lat", _BF16, (b, s_q, h, D_LATENT)), _ptr(lse, "lse", (torch.float32,), (b, s_q, h)),
         _stream()), "mla_decode_paged")

@@ -79,3 +79,64 @@ def test_large_score_growth_restarts_exactly(gpu_lib):
     res = host(run_path(gpu_lib, DevInputs(inp)))
     say("lse range", float(ref["lse"].min()), float(ref["lse"].max()))
     compare(res, ref, [0, 1], list(range(inp.h)), label="restart")
+
+
+def _dominant_key_inputs(h, s_q, targets, seed=11):
+    """Two sequences whose keys at ``targets`` [(b, t)] score far above everything before them in
+    their piece: the positional key of those rows is scaled up (their latent values, which form the
+    output, stay ordinary)."""
+    from mla_inputs import bf16_bits, f32
+    inp = make_inputs("tiny", seed=seed, seqlens=[3000, 700], h=h, s_q=s_q, causal=s_q > 1)
+    kv = f32(inp.kv_cache)
+    for b, t in targets:
+        kv[inp.block_table[b, t // 64], t % 64, 512:] *= 80.0
+    inp.kv_cache = bf16_bits(kv)
+    return inp
+
+
+def _largest_growth(inp, b, lo, t):
+    """Largest growth, in log2 units, of a row's score at key t over its maxima on keys [lo, lo + 32):
+    the first 32-token tile of the piece that starts at token lo."""
+    from mla_inputs import f32
+    rows = f32(inp.kv_cache)[inp.block_table[b, np.arange(lo, t + 1) // 64], np.arange(lo, t + 1) % 64]
+    rows = rows.astype(np.float64)
+    q_lat = O.absorb_q(f32(inp.q_nope[b:b + 1]), f32(inp.w_uk))[0]  # [s_q, h, 512]
+    s = inp.scale * (np.einsum("tc,jhc->jht", rows[:, :512], q_lat)
+                     + np.einsum("tc,jhc->jht", rows[:, 512:], f32(inp.q_pe[b]).astype(np.float64)))
+    first = s[:, :, :32].max(axis=2)
+    return float(((s[:, :, -1] - first) / np.log(2.0)).max())
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+@pytest.mark.parametrize("h", [64, 128])
+@pytest.mark.parametrize("mode", ["whole", "split"])
+def test_restart_in_row_block_kernel(gpu_lib, mode, h, s_q):
+    """The recompute of a piece whose scores outgrow the softmax reference (the row's first tile max)
+    in the row-block kernel (M = 64, 128, 256 rows), with the dominant key past the piece's first
+    tile: in a sequence held whole by one slot (finalised in place) and in one piece of a split
+    sequence (its partial then goes through the split merge). Every element against the oracle."""
+    from oracle import split_plan
+    F = gpu_lib.default_split_overhead(s_q, h)
+    if mode == "whole":
+        slots = 1
+        targets = [(0, 1000), (1, 500)]
+        starts = {0: 0, 1: 0}
+    else:
+        slots = 40
+        _, ns, pieces = split_plan.plan([3000, 700], slots, F)
+        targets, starts = [], {}
+        for b in (0, 1):
+            mine = [p for p in pieces if p[1] == b]
+            assert len(mine) >= 3
+            _, _, plo, phi, _ = mine[1]  # the second piece of the sequence
+            targets.append((b, plo * 64 + 40))  # in the piece's second tile
+            starts[b] = plo * 64
+    inp = _dominant_key_inputs(h, s_q, targets)
+    for b, t in targets:  # the premise: some row's growth passes the 64 (log2) slack
+        g = _largest_growth(inp, b, starts[b], t)
+        say("mode", mode, "h", h, "s_q", s_q, "seq", b, "key", t, "largest growth (log2)", round(g, 1))
+        assert g > 70.0
+    ref = O.decode_naive_inputs(inp)
+    res = host(run_path(gpu_lib, DevInputs(inp), slots=slots))
+    compare(res, ref, [0, 1], list(range(inp.h)), label=f"restart {mode} h={h} s_q={s_q}")
+    assert gpu_lib.take_device_error() == 0
