@@ -9,11 +9,16 @@ synthetic tensors already resident in HBM. To keep the 256 MB Infinity Cache
 from serving repeats, R copies of every input and output rotate, with R times
 the working set above 1 GiB.
 
-`value` is the wall time per step with each step replayed from a HIP graph
-(one graph per rotating input set, recorded through torch's graph capture on
-the library's stream), so no host launch gap sits between the kernels of a
-step; `eager_us_per_step` is the same steps launched eagerly, whose per-call
-hipEvents give `stage_us` and the decode call's roofline.
+`value` is the wall time per step over exactly --steps steps, each replayed
+from a HIP graph (one graph per rotating input set, recorded through torch's
+graph capture on the library's stream), so no host launch gap sits between the
+kernels of a step. Before the timed steps, untimed steps run for
+--warmup-seconds (the clock settles only under sustained load; reported as
+`warmup_s`) and then --warmup steps. `eager_us_per_step` is at least 50 of the
+same steps launched eagerly; hipEvents around each call give the medians in
+`stage_us` and the decode call's `decode_us` and roofline. With the default
+workload (full_heads) the matrix-bound multi_token workload is measured in the
+same run and reported under its own key.
 
 Prints one JSON line (rank 0, N = 1). Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config full_heads]
@@ -126,82 +131,74 @@ def time_append(mla, inp, sets, n: int):
             "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 5)}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, budget_s: float):
-    """Time the CPU oracle as it stands on a bounded sample and scale to one call."""
+    """Time the CPU oracle as it stands (NumPy fp32, naive expand-then-attend form) on a bounded sample
+    of the workload, with as many BLAS threads as this process may run on, and scale to one call."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from oracle import mla_oracle as O
+    cores = len(os.sched_getaffinity(0))
     order = np.argsort(inp.seqlens)
     seqs = [int(order[len(order) // 2])]  # a median-length sequence
-    heads = list(range(inp.h))
     done_heads = 0
-    t0 = time.perf_counter()
-    for hd in heads:  # one head at a time until the budget is spent
-        O.decode_naive_inputs(inp, seqs=seqs, heads=[hd])
-        done_heads += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for hd in range(inp.h):  # one head at a time until the budget is spent
+            O.decode_naive_inputs(inp, seqs=seqs, heads=[hd], dtype=np.float32)
+            done_heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
     L = np.maximum(inp.seqlens.astype(np.int64), 0)
     frac = float(L[seqs].sum()) * done_heads / (float(L.sum()) * inp.h)
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": dt / frac * 1e6, "unit": "us/call", "cores": int(threads), "kind": "oracle",
-            "sample": f"naive fp64 oracle on sequence {seqs[0]} (L={int(L[seqs[0]])}), {done_heads} of {inp.h} "
-                      f"heads, {dt:.1f} s, scaled by key-head count to the full call"}
+    return {"value": round(dt / frac * 1e6, 1), "unit": "us/call", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "sampled_fraction": round(frac, 6), "sample_s": round(dt, 2),
+            "sample": f"naive fp32 NumPy oracle on sequence {seqs[0]} (L={int(L[seqs[0]])}), {done_heads} of "
+                      f"{inp.h} heads ({frac:.4%} of the call's key-head pairs), {dt:.1f} s with {cores} BLAS "
+                      f"threads, scaled by key-head count to the full call"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    # the GPU reaches its steady clock only after about 100 steps (~15 ms) of
-    # load: with 10 warm-up steps the timed steps averaged 156 us against 140 us
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", default="full_heads")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--separate-plan", action="store_true",
-                    help="plan with mla_get_metadata and absorb with mla_absorb_q (two launches) instead of "
-                         "mla_absorb_q_with_plan")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time the steps as eager launches only (value = eager wall time per step)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="after the timed steps, run one plain elementwise copy (torch.neg) of MIB MiB so that "
-                         "hardware byte counters can be scaled against a kernel of known traffic")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library runs on one "
-              "GPU and does not shard the decode across GPUs)", file=sys.stderr)
-        sys.exit(2)
+def _dev_bf16(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
+
+def _dev_i32(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float):
+    """One workload: R rotating input sets resident in HBM; a time-based warm-up (the clock settles only
+    after about 100 steps of load), then ``warmup`` untimed steps; max(steps, 50) eager steps with
+    hipEvents around every call (their medians give the per-call times); then the same steps captured
+    in HIP graphs, ``warmup`` untimed replays and exactly ``steps`` timed replays (the step time)."""
     import numpy as np
     import torch
 
-    import mla_decode_paged_amd as mla
-    from mla_inputs import CONFIGS, make_inputs
-
-    torch.cuda.set_device(0)
-    mla.load()
-    inp = make_inputs(args.config, seed=args.seed)
-    work = algorithmic_work(inp)
-
-    def dev_bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-
-    def dev_i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
-
-    kv0 = dev_bf16(inp.kv_cache)
+    kv0 = _dev_bf16(inp.kv_cache)
     working = kv0.numel() * 2 + inp.b * inp.s_q * inp.h * (576 + 512 + 512) * 2
     R = max(1, math.ceil((1 << 30) / working))
     sets = []
     for r in range(R):
         sets.append(dict(
-            kv=kv0 if r == 0 else kv0.clone(), bt=dev_i32(inp.block_table), sl=dev_i32(inp.seqlens),
-            q_nope=dev_bf16(inp.q_nope), q_pe=dev_bf16(inp.q_pe), w_uk=dev_bf16(inp.w_uk),
-            w_uv=dev_bf16(inp.w_uv),
+            kv=kv0 if r == 0 else kv0.clone(), bt=_dev_i32(inp.block_table), sl=_dev_i32(inp.seqlens),
+            q_nope=_dev_bf16(inp.q_nope), q_pe=_dev_bf16(inp.q_pe), w_uk=_dev_bf16(inp.w_uk),
+            w_uv=_dev_bf16(inp.w_uv),
             q_lat=torch.empty((inp.b, inp.s_q, inp.h, 512), dtype=torch.bfloat16, device="cuda"),
             q_lo=torch.empty((inp.b, inp.s_q, inp.h, 512), dtype=torch.bfloat16, device="cuda"),
             o_lat=torch.empty((inp.b, inp.s_q, inp.h, 512), dtype=torch.bfloat16, device="cuda"),
@@ -244,19 +241,29 @@ def main():
             for k, a, b in stages + (("decode", 2, 3), ("up_v", 3, 4)):
                 ev[k].append((e[a], e[b]))
 
-    for i in range(args.warmup):
+    # time-based warm-up, then the requested warm-up steps
+    t0 = time.perf_counter()
+    n_time_warm = 0
+    while time.perf_counter() - t0 < warmup_s:
+        for _ in range(25):
+            step(n_time_warm, False)
+            n_time_warm += 1
+        torch.cuda.synchronize()
+    t_warm = time.perf_counter() - t0
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
+    n_ev = max(steps, 50)
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(n_ev):
         step(i, True)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    us_step_eager = (time.perf_counter() - t0) / n_ev * 1e6
     assert mla.take_device_error() == 0
-    us_step_eager = wall / args.steps * 1e6
+    per_call = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in ev.items()}
     # The same steps replayed from HIP graphs, one per rotating input set:
     # each step's launches are recorded once, so a replay has no host launch
-    # gaps between its kernels. The per-call events above give the stages.
+    # gaps between its kernels.
     us_step_graph = None
     if not args.no_graph:
         graphs = []
@@ -265,17 +272,94 @@ def main():
             with torch.cuda.graph(g):
                 step(r, False)
             graphs.append(g)
-        for i in range(max(args.warmup, R)):
+        for i in range(max(warmup, R)):
             graphs[i % R].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             graphs[i % R].replay()
         torch.cuda.synchronize()
-        us_step_graph = (time.perf_counter() - t0) / args.steps * 1e6
+        us_step_graph = (time.perf_counter() - t0) / steps * 1e6
         assert mla.take_device_error() == 0
         del graphs
-    append = time_append(mla, inp, sets, args.steps)
+    out = dict(sets=sets, R=R, slots=slots, us_step_eager=us_step_eager, us_step_graph=us_step_graph,
+               n_ev=n_ev, t_warm=t_warm, n_time_warm=n_time_warm,
+               median={k: float(np.median(v)) for k, v in per_call.items()},
+               mean={k: float(np.mean(v)) for k, v in per_call.items()})
+    return out
+
+
+def summary(inp, m, traffic, seed):
+    """Per-workload figures of the JSON line for one measure() result."""
+    work = algorithmic_work(inp)
+    t_dec = m["median"]["decode"] * 1e-6
+    achieved = work["bytes"] / t_dec / 1e9
+    tflops = work["flops"] / t_dec / 1e12
+    from mla_inputs import CONFIGS
+    cfg = CONFIGS[inp.name]
+    us_step = m["us_step_graph"] if m["us_step_graph"] is not None else m["us_step_eager"]
+    return {
+        "workload": f"{inp.name}: b={inp.b} h={inp.h} s_q={inp.s_q} causal={inp.causal} "
+                    f"seqlens={cfg['seqlens']} sum_L={int(inp.seqlens.sum())} page=64 row=576 bf16 seed={seed}",
+        "us_per_step": round(us_step, 3),
+        "step_mode": "hip_graph" if m["us_step_graph"] is not None else "eager",
+        "eager_us_per_step": round(m["us_step_eager"], 3),
+        "stage_us": {k: round(v, 3) for k, v in m["median"].items()},
+        "stage_us_mean": {k: round(v, 3) for k, v in m["mean"].items()},
+        "timed_calls": m["n_ev"],
+        "decode_us": round(m["median"]["decode"], 3),
+        "latent_kv_TBps": round(work["kv_bytes"] / t_dec / 1e12, 4),
+        "decode_TFLOPs": round(tflops, 2),
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
+        "roofline": roofline_entry(work, t_dec, traffic),
+        "num_slots": m["slots"], "rotating_copies": m["R"],
+        "warmup_s": round(m["t_warm"], 3), "warmup_time_steps": m["n_time_warm"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU reaches its steady clock only after about 100 steps (~15 ms) of
+    # load: besides the --warmup steps, untimed steps run for this long first
+    # (reported as warmup_s)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5)
+    ap.add_argument("--config", default="full_heads")
+    ap.add_argument("--extra", nargs="*", default=None,
+                    help="further workloads measured in the same run and reported under their own keys "
+                         "(default: multi_token, the matrix-bound case, when --config is full_heads)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-plan", action="store_true",
+                    help="plan with mla_get_metadata and absorb with mla_absorb_q (two launches) instead of "
+                         "mla_absorb_q_with_plan")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the steps as eager launches only (value = eager wall time per step)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run one plain elementwise copy (torch.neg) of MIB MiB so that "
+                         "hardware byte counters can be scaled against a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library runs on one "
+              "GPU and does not shard the decode across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    extra = args.extra if args.extra is not None else (["multi_token"] if args.config == "full_heads" else [])
+
+    import torch
+
+    import mla_decode_paged_amd as mla
+    from mla_inputs import make_inputs
+
+    torch.cuda.set_device(0)
+    mla.load()
+    inp = make_inputs(args.config, seed=args.seed)
+    m = measure(mla, inp, args, args.steps, args.warmup, args.warmup_seconds)
+    append = time_append(mla, inp, m["sets"], args.steps)
+    del m["sets"]
     if args.copy_calibration > 0:  # reads and writes exactly MIB MiB each
         src = torch.ones((args.copy_calibration << 18,), dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -283,32 +367,26 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    us = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in ev.items()}
-    us_step = us_step_graph if us_step_graph is not None else us_step_eager
-
-    t_dec = us["decode"] * 1e-6
-    achieved = work["bytes"] / t_dec / 1e9
-    tflops = work["flops"] / t_dec / 1e12
-    cfg = CONFIGS[args.config]
+    main_sum = summary(inp, m, recorded_traffic(args.config), args.seed)
+    us_step = main_sum["us_per_step"]
     line = {
-        "metric": METRIC, "value": round(us_step, 3), "unit": "us/call", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.config}: b={inp.b} h={inp.h} s_q={inp.s_q} causal={inp.causal} "
-                               f"seqlens={cfg['seqlens']} sum_L={int(inp.seqlens.sum())} page=64 row=576 bf16 "
-                               f"seed={args.seed}",
-                   "num_slots": slots, "rotating_copies": R},
-        "step_mode": "hip_graph" if us_step_graph is not None else "eager",
-        "eager_us_per_step": round(us_step_eager, 3),
-        "stage_us": {k: round(v, 3) for k, v in us.items()},
-        "decode_us": round(us["decode"], 3),
-        "append_kv": append,
-        "latent_kv_TBps": round(work["kv_bytes"] / t_dec / 1e12, 4),
-        "decode_TFLOPs": round(tflops, 2),
-        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
-        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
-        "roofline": roofline_entry(work, t_dec, recorded_traffic(args.config)),
+        "metric": METRIC, "value": us_step, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "warmup_s": main_sum["warmup_s"], "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": main_sum["workload"], "num_slots": main_sum["num_slots"],
+                   "rotating_copies": main_sum["rotating_copies"]},
     }
+    for k in ("step_mode", "eager_us_per_step", "stage_us", "stage_us_mean", "timed_calls", "decode_us",
+              "latent_kv_TBps", "decode_TFLOPs", "hbm_frac", "mfma_frac", "roofline", "warmup_time_steps"):
+        line[k] = main_sum[k]
+    line["append_kv"] = append
+    for name in extra:
+        torch.cuda.empty_cache()
+        xin = make_inputs(name, seed=args.seed)
+        xm = measure(mla, xin, args, args.steps, args.warmup, args.warmup_seconds)
+        del xm["sets"]
+        line[name] = summary(xin, xm, recorded_traffic(name), args.seed)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(line), flush=True)
