@@ -175,6 +175,36 @@ int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint
                      void* workspace, size_t workspace_bytes,
                      uint16_t* o_lat, float* lse, void* stream);
 
+/* Size of the device array mla_decode_paged_noalloc uses in place of a
+ * workspace: 72 MiB on every GPU the library runs on, held until the process
+ * ends. It covers mla_workspace_bytes(b, s_q, h, mla_num_slots(...)) for
+ * b = 128 sequences at s_q * h <= 256 rows and for 32 sequences of 1024 rows. */
+#define MLA_NOALLOC_SCRATCH_BYTES (72u << 20)
+
+/* mla_decode_paged_noalloc - mla_decode_paged for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc. It takes no workspace: the split
+ * partials go to a fixed array of MLA_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per GPU. The call itself allocates nothing; its first call on a
+ * device resolves that device's array address once.
+ *
+ * Arguments, outputs, results and error behaviour are those of
+ * mla_decode_paged (the outputs are bit-identical to that call's), without
+ * workspace and workspace_bytes. A shape whose
+ * mla_workspace_bytes(b, s_q, h, num_slots) exceeds MLA_NOALLOC_SCRATCH_BYTES
+ * returns MLA_ERR_WORKSPACE before anything is launched.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero). Calls that overlap on one
+ * GPU - on different streams, or from several host threads - race on it and
+ * must be ordered by the caller. */
+int mla_decode_paged_noalloc(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                             const uint16_t* kv_cache, int64_t num_pages,
+                             const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                             int b, int s_q, int h, float softmax_scale, int causal,
+                             const int32_t* tile_meta, const int32_t* num_splits, int num_slots,
+                             uint16_t* o_lat, float* lse, void* stream);
+
 /* mla_up_v - value up-projection per head (section 2.2: v = W_UV c, applied
  * after attention since the output is linear in c):
  * o[b, j, i, :] = o_lat[b, j, i, :] @ W_UV[i], fp32 accumulation, bf16 out.

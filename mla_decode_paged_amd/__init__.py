@@ -24,7 +24,7 @@ import os
 import torch
 
 __all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "absorb_q_with_plan",
-           "decode_paged",
+           "decode_paged", "decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
            "up_v", "gather_pages", "append_kv", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
            "SPLIT_OVERHEAD_FEW_ROWS", "SPLIT_OVERHEAD_ROW_BLOCKS", "default_split_overhead",
            "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE", "MLA_DEVERR_PAGE_ID",
@@ -35,6 +35,8 @@ PAGE_TOKENS, D_LATENT, D_ROPE, D_ROW, D_NOPE = 64, 512, 64, 576, 128
 # device error bits (MLA_DEVERR_* of include/mla.h)
 MLA_DEVERR_PAGE_ID, MLA_DEVERR_SEQ_TOO_LONG, MLA_DEVERR_SHORT_SEQ = 1, 2, 4
 META_WORDS = 8
+# MLA_NOALLOC_SCRATCH_BYTES of include/mla.h: the built-in scratch of decode_paged_noalloc
+NOALLOC_SCRATCH_BYTES = 72 << 20
 # Fixed cost of one sequence piece in the split plan, in pages: a piece's
 # query loads, first-tile latency, epilogue stores and share of the merge,
 # measured on MI355X against the per-page cost of the kernel that runs it.
@@ -75,6 +77,8 @@ def load():
         "mla_absorb_q_with_plan": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _P]),
         "mla_decode_paged": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
                                   _P, _P, _P]),
+        "mla_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I,
+                                          _P, _P, _P]),
         "mla_up_v": (_I, [_P, _P, _P, _I, _I, _I, _P]),
         "mla_gather_pages": (_I, [_P, _I64, _P, _I, _P, _I, _P, _P, _P]),
         "mla_append_kv": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _P]),
@@ -238,6 +242,34 @@ def decode_paged(q_lat, q_pe, kv_cache, block_table, cache_seqlens, tile_meta, n
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(o_lat, "o_lat", _BF16, (b, s_q, h, D_LATENT)), _ptr(lse, "lse", (torch.float32,), (b, s_q, h)),
         _stream()), "mla_decode_paged")
+    return o_lat, lse
+
+
+def decode_paged_noalloc(q_lat, q_pe, kv_cache, block_table, cache_seqlens, tile_meta, num_splits, softmax_scale,
+                         causal, q_lat_lo=None, out=None):
+    """decode_paged without a workspace: the split partials use the library's fixed per-GPU scratch
+    (mla_decode_paged_noalloc). Pass ``out`` to allocate nothing at all."""
+    if q_lat.dim() != 4 or tile_meta.dim() != 2 or block_table.dim() != 2:
+        raise MLAError(f"q_lat must be [b, s_q, h, {D_LATENT}], tile_meta [slots, {META_WORDS}] and "
+                       "block_table [b, max_blocks]")
+    b, s_q, h, _ = q_lat.shape
+    slots = tile_meta.shape[0]
+    dev = q_lat.device
+    if out is None:
+        o_lat = torch.empty((b, s_q, h, D_LATENT), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((b, s_q, h), dtype=torch.float32, device=dev)
+    else:
+        o_lat, lse = out
+    if kv_cache.dim() != 3 or tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_ROW):
+        raise MLAError(f"kv_cache must be [num_pages, {PAGE_TOKENS}, {D_ROW}]")
+    _check(load().mla_decode_paged_noalloc(
+        _ptr(q_lat, "q_lat", _BF16, (b, s_q, h, D_LATENT)), _ptr(q_lat_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)),
+        _ptr(q_pe, "q_pe", _BF16, (b, s_q, h, D_ROPE)), _ptr(kv_cache, "kv_cache", _BF16), kv_cache.shape[0],
+        _ptr(block_table, "block_table", _I32, (b, block_table.shape[1])), block_table.shape[1],
+        _ptr(cache_seqlens, "cache_seqlens", _I32, (b,)), b, s_q, h, float(softmax_scale), int(bool(causal)),
+        _ptr(tile_meta, "tile_meta", _I32, (slots, META_WORDS)), _ptr(num_splits, "num_splits", _I32, (b + 1,)),
+        slots, _ptr(o_lat, "o_lat", _BF16, (b, s_q, h, D_LATENT)),
+        _ptr(lse, "lse", (torch.float32,), (b, s_q, h)), _stream()), "mla_decode_paged_noalloc")
     return o_lat, lse
 
 

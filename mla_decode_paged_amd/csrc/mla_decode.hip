@@ -50,6 +50,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "mla_device.h"
 #include "mla_host.h"
@@ -1083,37 +1084,39 @@ extern "C" size_t mla_workspace_bytes(int b, int s_q, int h, int num_slots) {
   return round256(splits * M * kDLat * 2) + 2 * round256(splits * M * sizeof(float));
 }
 
-extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
-                                const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
-                                int max_blocks, const int32_t* cache_seqlens, int b, int s_q, int h,
-                                float softmax_scale, int causal, const int32_t* tile_meta,
-                                const int32_t* num_splits, int num_slots, void* workspace,
-                                size_t workspace_bytes, uint16_t* o_lat, float* lse, void* stream) {
-  const char* fn = "mla_decode_paged";
-  if (!q_lat || !q_pe || !kv_cache || !block_table || !cache_seqlens || !tile_meta || !num_splits ||
-      !workspace || !o_lat || !lse)
+// Host checks shared by both decode entry points (everything but the workspace).
+static int check_decode_args(const char* fn, const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                             const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
+                             int max_blocks, const int32_t* cache_seqlens, int b, int s_q, int h,
+                             float softmax_scale, const int32_t* tile_meta, const int32_t* num_splits,
+                             int num_slots, uint16_t* o_lat, float* lse) {
+  if (!q_lat || !q_pe || !kv_cache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !o_lat ||
+      !lse)
     return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
   if (int rc = check_shape(fn, b, s_q, h)) return rc;
   if (num_pages < 1 || max_blocks < 1 || num_slots < 1)
     return set_error(MLA_ERR_INVALID_ARG, "%s: num_pages, max_blocks and num_slots must be >= 1", fn);
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return set_error(MLA_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", fn);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return set_error(MLA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
-  const size_t need = mla_workspace_bytes(b, s_q, h, num_slots);
-  if (workspace_bytes < need)
-    return set_error(MLA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
   for (const void* p : {(const void*)q_lat, (const void*)q_pe, (const void*)kv_cache, (const void*)o_lat})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
       return set_error(MLA_ERR_INVALID_ARG, "%s: bf16 tensors must be 16-byte aligned", fn);
   if (q_lat_lo && reinterpret_cast<uintptr_t>(q_lat_lo) % 16 != 0)
     return set_error(MLA_ERR_INVALID_ARG, "%s: q_lat_lo must be 16-byte aligned", fn);
+  return MLA_OK;
+}
 
+// Launches of one decode call (arguments already checked; `ws` holds at least
+// mla_workspace_bytes(b, s_q, h, num_slots) bytes, 256-byte aligned).
+static int decode_launch(const char* fn, const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                         const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table, int max_blocks,
+                         const int32_t* cache_seqlens, int b, int s_q, int h, float softmax_scale, int causal,
+                         const int32_t* tile_meta, const int32_t* num_splits, int num_slots, char* ws,
+                         uint16_t* o_lat, float* lse, void* stream) {
   const int M = s_q * h;
   const int nw = rows_per_wg_waves(M);
   const int R = (M + nw * 32 - 1) / (nw * 32);
   const size_t M_ = (size_t)M, splits = (size_t)b + num_slots;
-  char* ws = static_cast<char*>(workspace);
   DecodeParams P;
   P.q_lat = q_lat;
   P.q_lat_lo = q_lat_lo;
@@ -1160,6 +1163,86 @@ extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo,
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
     return set_error(MLA_ERR_HIP, "%s: combine launch failed: %s", fn, hipGetErrorString(e));
   return clear_error();
+}
+
+extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                                const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                int max_blocks, const int32_t* cache_seqlens, int b, int s_q, int h,
+                                float softmax_scale, int causal, const int32_t* tile_meta,
+                                const int32_t* num_splits, int num_slots, void* workspace,
+                                size_t workspace_bytes, uint16_t* o_lat, float* lse, void* stream) {
+  const char* fn = "mla_decode_paged";
+  if (!workspace) return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+  if (int rc = check_decode_args(fn, q_lat, q_lat_lo, q_pe, kv_cache, num_pages, block_table, max_blocks,
+                                 cache_seqlens, b, s_q, h, softmax_scale, tile_meta, num_splits, num_slots, o_lat,
+                                 lse))
+    return rc;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = mla_workspace_bytes(b, s_q, h, num_slots);
+  if (workspace_bytes < need)
+    return set_error(MLA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  return decode_launch(fn, q_lat, q_lat_lo, q_pe, kv_cache, num_pages, block_table, max_blocks, cache_seqlens, b,
+                       s_q, h, softmax_scale, causal, tile_meta, num_splits, num_slots,
+                       static_cast<char*>(workspace), o_lat, lse, stream);
+}
+
+// Scratch of mla_decode_paged_noalloc: one fixed array per GPU, in the
+// library's device code object, in place of the caller's workspace. In host
+// code `scratch` names a host-side stand-in, not device memory: the device
+// address comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch` per device id (null until resolved)
+}  // namespace
+
+static int scratch_for_current_device(const char* fn, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return set_error(MLA_ERR_HIP, "%s: cannot query the current device", fn);
+  if (dev >= kMaxDevices)
+    return set_error(MLA_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices this call supports", fn, dev,
+                     kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_error(MLA_ERR_HIP, "%s: cannot resolve the scratch array on device %d: %s", fn, dev,
+                       hipGetErrorString(e));
+    if (reinterpret_cast<uintptr_t>(p) % 256 != 0)
+      return set_error(MLA_ERR_HIP, "%s: the scratch array on device %d is not 256-byte aligned", fn, dev);
+    g_scratch_dev[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_dev[dev]);
+  return MLA_OK;
+}
+
+extern "C" int mla_decode_paged_noalloc(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                                        const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
+                                        int max_blocks, const int32_t* cache_seqlens, int b, int s_q, int h,
+                                        float softmax_scale, int causal, const int32_t* tile_meta,
+                                        const int32_t* num_splits, int num_slots, uint16_t* o_lat, float* lse,
+                                        void* stream) {
+  const char* fn = "mla_decode_paged_noalloc";
+  if (int rc = check_decode_args(fn, q_lat, q_lat_lo, q_pe, kv_cache, num_pages, block_table, max_blocks,
+                                 cache_seqlens, b, s_q, h, softmax_scale, tile_meta, num_splits, num_slots, o_lat,
+                                 lse))
+    return rc;
+  const size_t need = mla_workspace_bytes(b, s_q, h, num_slots);
+  if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return set_error(MLA_ERR_WORKSPACE,
+                     "%s: this shape needs %zu bytes of split partials (b=%d, s_q=%d, h=%d, num_slots=%d), more "
+                     "than the %zu-byte built-in scratch; use mla_decode_paged with a workspace",
+                     fn, need, b, s_q, h, num_slots, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if (int rc = scratch_for_current_device(fn, &ws)) return rc;
+  return decode_launch(fn, q_lat, q_lat_lo, q_pe, kv_cache, num_pages, block_table, max_blocks, cache_seqlens, b,
+                       s_q, h, softmax_scale, causal, tile_meta, num_splits, num_slots, ws, o_lat, lse, stream);
 }
 
 extern "C" int mla_gather_pages(const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,

@@ -135,3 +135,39 @@ def test_absorb_with_plan_rejects(lib, kw, code, msg):
     """The combined call applies the checks of both calls before anything is launched."""
     assert _absorb_plan(lib, **kw) == code
     assert msg in lib.mla_last_error().decode()
+
+
+def _noalloc(lib, **kw):
+    a = dict(q_lat=FAKE, q_lat_lo=None, q_pe=FAKE, kv=FAKE, num_pages=10, bt=FAKE, max_blocks=4, sl=FAKE, b=2,
+             s_q=1, h=16, scale=0.07, causal=0, meta=FAKE, ns=FAKE, slots=8, o=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_paged_noalloc(a["q_lat"], a["q_lat_lo"], a["q_pe"], a["kv"], a["num_pages"], a["bt"],
+                                        a["max_blocks"], a["sl"], a["b"], a["s_q"], a["h"], a["scale"],
+                                        a["causal"], a["meta"], a["ns"], a["slots"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q_lat=None), INVALID, "NULL"),
+    (dict(lse=None), INVALID, "NULL"),
+    (dict(h=48), UNSUPPORTED, "h must be"),
+    (dict(scale=-1.0), INVALID, "softmax_scale"),
+    (dict(o=ctypes.c_void_p((1 << 20) + 8)), INVALID, "aligned"),
+    # 8192 sequences of 1024 rows: far more split partials than the built-in scratch holds
+    (dict(b=8192, s_q=8, h=128, slots=256), WORKSPACE, "built-in scratch"),
+])
+def test_noalloc_rejects(lib, kw, code, msg):
+    """The no-allocation decode entry applies the decode checks and refuses shapes whose split partials
+    exceed its fixed scratch, before it touches the device."""
+    assert _noalloc(lib, **kw) == code
+    assert msg in lib.mla_last_error().decode()
+
+
+def test_noalloc_scratch_size_matches_the_header(lib):
+    import mla_decode_paged_amd as mla
+    text = open(HEADER).read()
+    m = re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mla.NOALLOC_SCRATCH_BYTES
+    # the largest default-slot workspaces of the benchmark workloads fit
+    for b, s_q, h, slots in [(128, 1, 32, 256), (128, 1, 128, 256), (16, 1, 128, 256), (128, 2, 128, 128),
+                             (32, 8, 128, 32)]:
+        assert lib.mla_workspace_bytes(b, s_q, h, slots) <= mla.NOALLOC_SCRATCH_BYTES
