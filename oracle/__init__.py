@@ -15,4 +15,4 @@ Contents
 
 Every function is pinned by a CPU test; none is "parity unpinned".
 """
-from . import mla_oracle, split_plan  # noqa: F401
+from . import kv_quant, mla_oracle, split_plan  # noqa: F401
