@@ -40,13 +40,18 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def algorithmic_work(inp):
+# bytes a cached token occupies: a bf16 row of 576 values, or a quantised row (512 e4m3 codes,
+# 64 bf16 key values and its fp32 scale)
+TOKEN_BYTES = {"bf16": 1152, "fp8": 512 + 128 + 4}
+
+
+def algorithmic_work(inp, kv="bf16"):
     """Bytes and flops the decode call must move and compute (no re-reads, no partials)."""
     import numpy as np
     L = np.maximum(inp.seqlens.astype(np.int64), 0)
     rows = inp.b * inp.s_q * inp.h
     pages = (L + 63) // 64
-    kv_bytes = int(L.sum()) * 1152
+    kv_bytes = int(L.sum()) * TOKEN_BYTES[kv]
     q_bytes = rows * (512 + 64) * 2
     out_bytes = rows * (512 * 2 + 4)
     int_bytes = 4 * int(pages.sum()) + 4 * inp.b
@@ -102,7 +107,7 @@ def recorded_traffic(config: str):
     return int(m.group(2))
 
 
-def time_append(mla, inp, sets, n: int):
+def time_append(mla, inp, sets, n: int, kv: str = "bf16"):
     """The step's cache append (mla_append_kv) on the same workload, after the timed steps:
     hipEvent time per call over back-to-back calls and its HBM rate (new rows read and written
     once, plus ints)."""
@@ -111,8 +116,9 @@ def time_append(mla, inp, sets, n: int):
 
     from mla_inputs import make_new_rows
     new = torch.from_numpy(make_new_rows(inp, seed=1).view(np.int16)).view(torch.bfloat16).cuda()
+    append = mla.append_kv_fp8 if kv == "fp8" else mla.append_kv  # the quantised cache quantises on append
     for s in sets[:2]:
-        mla.append_kv(new, s["kv"], s["bt"], s["sl"])
+        append(new, s["kv"], s["bt"], s["sl"])
     torch.cuda.synchronize()
     # The kernel is far shorter than one host-side launch, so the calls are queued behind a
     # sleeping kernel first: the events then see back-to-back launches, not host latency.
@@ -121,12 +127,12 @@ def time_append(mla, inp, sets, n: int):
     e0.record()
     for i in range(n):
         s = sets[i % len(sets)]
-        mla.append_kv(new, s["kv"], s["bt"], s["sl"])
+        append(new, s["kv"], s["bt"], s["sl"])
     e1.record()
     torch.cuda.synchronize()
     assert mla.take_device_error() == 0
     us = e0.elapsed_time(e1) * 1e3 / n
-    nbytes = 2 * inp.b * inp.s_q * 1152 + 4 * inp.b * (1 + inp.s_q)
+    nbytes = inp.b * inp.s_q * (1152 + TOKEN_BYTES[kv]) + 4 * inp.b * (1 + inp.s_q)
     return {"us": round(us, 3), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
             "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 5)}
 
@@ -182,7 +188,7 @@ def _dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
-def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float):
+def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float, kv: str = "bf16"):
     """One workload: R rotating input sets resident in HBM; a time-based warm-up (the clock settles only
     after about 100 steps of load), then ``warmup`` untimed steps; max(steps, 50) eager steps with
     hipEvents around every call (their medians give the per-call times); then the same steps captured
@@ -191,8 +197,12 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float):
     import torch
 
     kv0 = _dev_bf16(inp.kv_cache)
-    working = kv0.numel() * 2 + inp.b * inp.s_q * inp.h * (576 + 512 + 512) * 2
+    if kv == "fp8":  # the quantised cache, converted on the GPU
+        kv0 = mla.quantize_pages(kv0)
+        torch.cuda.synchronize()
+    working = kv0.numel() * kv0.element_size() + inp.b * inp.s_q * inp.h * (576 + 512 + 512) * 2
     R = max(1, math.ceil((1 << 30) / working))
+    decode = mla.decode_paged_fp8 if kv == "fp8" else mla.decode_paged
     sets = []
     for r in range(R):
         sets.append(dict(
@@ -230,8 +240,8 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float):
                 e[1].record()
         if timed:
             e[2].record()
-        mla.decode_paged(s["q_lat"], s["q_pe"], s["kv"], s["bt"], s["sl"], meta, ns, inp.scale, inp.causal,
-                         q_lat_lo=s["q_lo"], workspace=ws, out=(s["o_lat"], s["lse"]))
+        decode(s["q_lat"], s["q_pe"], s["kv"], s["bt"], s["sl"], meta, ns, inp.scale, inp.causal,
+               q_lat_lo=s["q_lo"], workspace=ws, out=(s["o_lat"], s["lse"]))
         if timed:
             e[3].record()
         mla.up_v(s["o_lat"], s["w_uv"], out=s["o"])
@@ -289,18 +299,23 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float):
     return out
 
 
-def summary(inp, m, traffic, seed):
+def summary(inp, m, traffic, seed, kv="bf16"):
     """Per-workload figures of the JSON line for one measure() result."""
-    work = algorithmic_work(inp)
+    work = algorithmic_work(inp, kv)
     t_dec = m["median"]["decode"] * 1e-6
     achieved = work["bytes"] / t_dec / 1e9
     tflops = work["flops"] / t_dec / 1e12
     from mla_inputs import CONFIGS
     cfg = CONFIGS[inp.name]
     us_step = m["us_step_graph"] if m["us_step_graph"] is not None else m["us_step_eager"]
+    lens = cfg["seqlens"]
+    if len(set(inp.seqlens.tolist())) == 1 and lens != ("all", int(inp.seqlens[0])):  # a --seqlen point
+        lens = ("all", int(inp.seqlens[0]))
+    cache = "bf16 576-wide rows" if kv == "bf16" else "quantised rows (e4m3 latent + bf16 key + fp32 scale, 644 B)"
     return {
         "workload": f"{inp.name}: b={inp.b} h={inp.h} s_q={inp.s_q} causal={inp.causal} "
-                    f"seqlens={cfg['seqlens']} sum_L={int(inp.seqlens.sum())} page=64 row=576 bf16 seed={seed}",
+                    f"seqlens={lens} sum_L={int(inp.seqlens.sum())} page=64 cache={cache} seed={seed}",
+        "kv_cache": kv,
         "us_per_step": round(us_step, 3),
         "step_mode": "hip_graph" if m["us_step_graph"] is not None else "eager",
         "eager_us_per_step": round(m["us_step_eager"], 3),
@@ -329,8 +344,14 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=0.5)
     ap.add_argument("--config", default="full_heads")
     ap.add_argument("--extra", nargs="*", default=None,
-                    help="further workloads measured in the same run and reported under their own keys "
-                         "(default: multi_token, the matrix-bound case, when --config is full_heads)")
+                    help="further workloads measured in the same run and reported under their own keys, "
+                         "name or name:fp8 (default with --config full_heads: multi_token, the matrix-bound "
+                         "case, and tp_share, the HBM-bound tensor-parallel share, with both caches)")
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+                    help="cache format of the main workload: bf16 rows or the quantised page format "
+                         "(mla_decode_paged_fp8; at most 32 query rows per sequence)")
+    ap.add_argument("--seqlen", type=int, default=0,
+                    help="give every sequence of the main workload this length (a length sweep point)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -347,7 +368,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library runs on one "
               "GPU and does not shard the decode across GPUs)", file=sys.stderr)
         sys.exit(2)
-    extra = args.extra if args.extra is not None else (["multi_token"] if args.config == "full_heads" else [])
+    extra = args.extra if args.extra is not None else \
+        (["multi_token", "tp_share", "tp_share:fp8"] if args.config == "full_heads" else [])
 
     import torch
 
@@ -356,9 +378,13 @@ def main():
 
     torch.cuda.set_device(0)
     mla.load()
-    inp = make_inputs(args.config, seed=args.seed)
-    m = measure(mla, inp, args, args.steps, args.warmup, args.warmup_seconds)
-    append = time_append(mla, inp, m["sets"], args.steps)
+    if args.seqlen > 0:
+        from mla_inputs import CONFIGS
+        inp = make_inputs(args.config, seed=args.seed, seqlens=[args.seqlen] * CONFIGS[args.config]["b"])
+    else:
+        inp = make_inputs(args.config, seed=args.seed)
+    m = measure(mla, inp, args, args.steps, args.warmup, args.warmup_seconds, kv=args.kv)
+    append = time_append(mla, inp, m["sets"], args.steps, kv=args.kv)
     del m["sets"]
     if args.copy_calibration > 0:  # reads and writes exactly MIB MiB each
         src = torch.ones((args.copy_calibration << 18,), dtype=torch.float32, device="cuda")
@@ -367,7 +393,8 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    main_sum = summary(inp, m, recorded_traffic(args.config), args.seed)
+    main_sum = summary(inp, m, recorded_traffic(args.config + ("_fp8" if args.kv == "fp8" else "")) if
+                       args.seqlen == 0 else None, args.seed, kv=args.kv)
     us_step = main_sum["us_per_step"]
     line = {
         "metric": METRIC, "value": us_step, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
@@ -382,10 +409,13 @@ def main():
     line["append_kv"] = append
     for name in extra:
         torch.cuda.empty_cache()
-        xin = make_inputs(name, seed=args.seed)
-        xm = measure(mla, xin, args, args.steps, args.warmup, args.warmup_seconds)
+        cfg_name, _, fmt = name.partition(":")
+        fmt = fmt or "bf16"
+        xin = make_inputs(cfg_name, seed=args.seed)
+        xm = measure(mla, xin, args, args.steps, args.warmup, args.warmup_seconds, kv=fmt)
         del xm["sets"]
-        line[name] = summary(xin, xm, recorded_traffic(name), args.seed)
+        line[name.replace(":", "_")] = summary(xin, xm, recorded_traffic(cfg_name + ("_fp8" if fmt == "fp8" else "")),
+                                               args.seed, kv=fmt)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

@@ -54,6 +54,17 @@ extern "C" {
 #define MLA_D_ROPE 64
 #define MLA_D_ROW 576
 #define MLA_D_NOPE 128
+/* Quantised cache page ("DeepSeek-V3 Multi-head Latent Attention (MLA) 深度工程",
+ * section 7.2 stores the latent in 8 bits; the format below is this library's
+ * reading): 64 rows of MLA_FP8_ROW_BYTES bytes - the 512 latent values as OCP
+ * fp8 e4m3 codes, then the 64 positional-key values as bf16 - followed by the
+ * 64 per-token scales as fp32, in token order. Row t stands for
+ * c_t = e4m3(code) * scale_t and k_pe_t as stored; scale_t = 2^e_t with e_t the
+ * smallest integer such that max |c_t| <= 448 * 2^e_t, but at least -126 (an
+ * all-zero row has scale 1). */
+#define MLA_FP8_ROW_BYTES 640
+#define MLA_FP8_SCALES_OFFSET (64 * MLA_FP8_ROW_BYTES)
+#define MLA_FP8_PAGE_BYTES (MLA_FP8_SCALES_OFFSET + 64 * 4)
 /* int32 words per slot in tile_meta */
 #define MLA_META_WORDS 8
 /* Largest batch the planner accepts. */
@@ -250,6 +261,43 @@ int mla_gather_pages(const uint16_t* kv_cache, int64_t num_pages, const int32_t*
 int mla_append_kv(const uint16_t* new_rows, uint16_t* kv_cache, int64_t num_pages,
                   const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
                   int b, int s_q, void* stream);
+
+/* mla_quantize_pages - convert a bf16 paged cache into the quantised page
+ * format (MLA_FP8_PAGE_BYTES per page; see MLA_FP8_ROW_BYTES): per row, the
+ * scale 2^e, the latent values divided by it (exact) and rounded to the
+ * nearest e4m3 code (ties to even), the positional key copied.
+ *
+ * kv_cache  bf16 [num_pages, 64, 576] with finite values
+ * kv_fp8    uint8 [num_pages, MLA_FP8_PAGE_BYTES] out, 16-byte aligned
+ * num_pages >= 1. Every page is converted, in place of the caller's rows. */
+int mla_quantize_pages(const uint16_t* kv_cache, int64_t num_pages, uint8_t* kv_fp8, void* stream);
+
+/* mla_append_kv_fp8 - mla_append_kv into a quantised cache: each new row is
+ * quantised as by mla_quantize_pages and its 640 row bytes and scale are
+ * written at token L_b - s_q + j of sequence b. Arguments, checks and device
+ * error bits as for mla_append_kv; kv_fp8 is uint8 [num_pages,
+ * MLA_FP8_PAGE_BYTES], 16-byte aligned. Only the destination rows and scales
+ * change. */
+int mla_append_kv_fp8(const uint16_t* new_rows, uint8_t* kv_fp8, int64_t num_pages,
+                      const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                      int b, int s_q, void* stream);
+
+/* mla_decode_paged_fp8 - mla_decode_paged over a quantised cache. The result
+ * is the decode of the cache the quantised pages stand for (latent values
+ * e4m3(code) * scale, positional keys as stored): scores apply each token's
+ * scale to its latent dot product, and the probabilities that weight its
+ * latent row carry the scale too. Arguments, outputs, workspace and error
+ * behaviour are those of mla_decode_paged, with kv_fp8 uint8 [num_pages,
+ * MLA_FP8_PAGE_BYTES] (16-byte aligned) in place of kv_cache. Built for at
+ * most 32 query rows per sequence (s_q * h <= 32: a tensor-parallel share of
+ * the heads): larger shapes return MLA_ERR_UNSUPPORTED. */
+int mla_decode_paged_fp8(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                         const uint8_t* kv_fp8, int64_t num_pages,
+                         const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                         int b, int s_q, int h, float softmax_scale, int causal,
+                         const int32_t* tile_meta, const int32_t* num_splits, int num_slots,
+                         void* workspace, size_t workspace_bytes,
+                         uint16_t* o_lat, float* lse, void* stream);
 
 /* Device error word: returns in *bits (host) the MLA_DEVERR_* bits kernels
  * set since the last call, then clears them. Synchronises the device. The

@@ -24,7 +24,8 @@ import os
 import torch
 
 __all__ = ["load", "last_error", "num_slots", "workspace_bytes", "get_metadata", "absorb_q", "absorb_q_with_plan",
-           "decode_paged", "decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "decode_paged", "decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES", "quantize_pages", "append_kv_fp8",
+           "decode_paged_fp8", "FP8_ROW_BYTES", "FP8_PAGE_BYTES",
            "up_v", "gather_pages", "append_kv", "take_device_error", "MLAError", "LIB_PATH", "SPLIT_OVERHEAD",
            "SPLIT_OVERHEAD_FEW_ROWS", "SPLIT_OVERHEAD_ROW_BLOCKS", "default_split_overhead",
            "PAGE_TOKENS", "D_LATENT", "D_ROPE", "D_ROW", "D_NOPE", "MLA_DEVERR_PAGE_ID",
@@ -35,6 +36,9 @@ PAGE_TOKENS, D_LATENT, D_ROPE, D_ROW, D_NOPE = 64, 512, 64, 576, 128
 # device error bits (MLA_DEVERR_* of include/mla.h)
 MLA_DEVERR_PAGE_ID, MLA_DEVERR_SEQ_TOO_LONG, MLA_DEVERR_SHORT_SEQ = 1, 2, 4
 META_WORDS = 8
+# quantised cache page (MLA_FP8_* of include/mla.h): 64 rows of 640 bytes, then 64 fp32 scales
+FP8_ROW_BYTES = 640
+FP8_PAGE_BYTES = 64 * FP8_ROW_BYTES + 64 * 4
 # MLA_NOALLOC_SCRATCH_BYTES of include/mla.h: the built-in scratch of decode_paged_noalloc
 NOALLOC_SCRATCH_BYTES = 72 << 20
 # Fixed cost of one sequence piece in the split plan, in pages: a piece's
@@ -79,6 +83,10 @@ def load():
                                   _P, _P, _P]),
         "mla_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I,
                                           _P, _P, _P]),
+        "mla_decode_paged_fp8": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
+                                      _P, _P, _P]),
+        "mla_quantize_pages": (_I, [_P, _I64, _P, _P]),
+        "mla_append_kv_fp8": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _P]),
         "mla_up_v": (_I, [_P, _P, _P, _I, _I, _I, _P]),
         "mla_gather_pages": (_I, [_P, _I64, _P, _I, _P, _I, _P, _P, _P]),
         "mla_append_kv": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _P]),
@@ -270,6 +278,64 @@ def decode_paged_noalloc(q_lat, q_pe, kv_cache, block_table, cache_seqlens, tile
         _ptr(tile_meta, "tile_meta", _I32, (slots, META_WORDS)), _ptr(num_splits, "num_splits", _I32, (b + 1,)),
         slots, _ptr(o_lat, "o_lat", _BF16, (b, s_q, h, D_LATENT)),
         _ptr(lse, "lse", (torch.float32,), (b, s_q, h)), _stream()), "mla_decode_paged_noalloc")
+    return o_lat, lse
+
+
+def quantize_pages(kv_cache, out=None):
+    """bf16 paged cache [num_pages, 64, 576] -> the quantised page format, uint8 [num_pages, FP8_PAGE_BYTES]."""
+    if kv_cache.dim() != 3 or tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_ROW):
+        raise MLAError(f"kv_cache must be [num_pages, {PAGE_TOKENS}, {D_ROW}]")
+    n = kv_cache.shape[0]
+    kv8 = out if out is not None else torch.empty((n, FP8_PAGE_BYTES), dtype=torch.uint8, device=kv_cache.device)
+    _check(load().mla_quantize_pages(_ptr(kv_cache, "kv_cache", _BF16), n,
+                                     _ptr(kv8, "kv_fp8", (torch.uint8,), (n, FP8_PAGE_BYTES)), _stream()),
+           "mla_quantize_pages")
+    return kv8
+
+
+def append_kv_fp8(new_rows, kv_fp8, block_table, cache_seqlens):
+    """append_kv into a quantised cache uint8 [num_pages, FP8_PAGE_BYTES] (each new row quantised)."""
+    if new_rows.dim() != 3 or new_rows.shape[2] != D_ROW:
+        raise MLAError(f"new_rows has shape {tuple(new_rows.shape)}, expected [b, s_q, {D_ROW}]")
+    if kv_fp8.dim() != 2 or kv_fp8.shape[1] != FP8_PAGE_BYTES or block_table.dim() != 2:
+        raise MLAError(f"kv_fp8 must be [num_pages, {FP8_PAGE_BYTES}] and block_table [b, max_blocks]")
+    b, s_q = new_rows.shape[0], new_rows.shape[1]
+    _check(load().mla_append_kv_fp8(_ptr(new_rows, "new_rows", _BF16), _ptr(kv_fp8, "kv_fp8", (torch.uint8,)),
+                                    kv_fp8.shape[0], _ptr(block_table, "block_table", _I32, (b, block_table.shape[1])),
+                                    block_table.shape[1], _ptr(cache_seqlens, "cache_seqlens", _I32, (b,)), b, s_q,
+                                    _stream()), "mla_append_kv_fp8")
+    return kv_fp8
+
+
+def decode_paged_fp8(q_lat, q_pe, kv_fp8, block_table, cache_seqlens, tile_meta, num_splits, softmax_scale,
+                     causal, q_lat_lo=None, workspace=None, out=None):
+    """decode_paged over a quantised cache uint8 [num_pages, FP8_PAGE_BYTES] (at most 32 query rows per
+    sequence): (o_lat bf16 [b, s_q, h, 512], lse fp32 [b, s_q, h])."""
+    if q_lat.dim() != 4 or tile_meta.dim() != 2 or block_table.dim() != 2:
+        raise MLAError(f"q_lat must be [b, s_q, h, {D_LATENT}], tile_meta [slots, {META_WORDS}] and "
+                       "block_table [b, max_blocks]")
+    if kv_fp8.dim() != 2 or kv_fp8.shape[1] != FP8_PAGE_BYTES:
+        raise MLAError(f"kv_fp8 must be [num_pages, {FP8_PAGE_BYTES}]")
+    b, s_q, h, _ = q_lat.shape
+    slots = tile_meta.shape[0]
+    dev = q_lat.device
+    need = workspace_bytes(b, s_q, h, slots)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if out is None:
+        o_lat = torch.empty((b, s_q, h, D_LATENT), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((b, s_q, h), dtype=torch.float32, device=dev)
+    else:
+        o_lat, lse = out
+    _check(load().mla_decode_paged_fp8(
+        _ptr(q_lat, "q_lat", _BF16, (b, s_q, h, D_LATENT)), _ptr(q_lat_lo, "q_lat_lo", _BF16, (b, s_q, h, D_LATENT)),
+        _ptr(q_pe, "q_pe", _BF16, (b, s_q, h, D_ROPE)), _ptr(kv_fp8, "kv_fp8", (torch.uint8,)), kv_fp8.shape[0],
+        _ptr(block_table, "block_table", _I32, (b, block_table.shape[1])), block_table.shape[1],
+        _ptr(cache_seqlens, "cache_seqlens", _I32, (b,)), b, s_q, h, float(softmax_scale), int(bool(causal)),
+        _ptr(tile_meta, "tile_meta", _I32, (slots, META_WORDS)), _ptr(num_splits, "num_splits", _I32, (b + 1,)),
+        slots, _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(o_lat, "o_lat", _BF16, (b, s_q, h, D_LATENT)), _ptr(lse, "lse", (torch.float32,), (b, s_q, h)),
+        _stream()), "mla_decode_paged_fp8")
     return o_lat, lse
 
 

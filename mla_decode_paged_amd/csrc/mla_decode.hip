@@ -51,6 +51,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "mla_device.h"
 #include "mla_host.h"
@@ -89,6 +90,7 @@ struct DecodeParams {
   const uint16_t* q_lat_lo;
   const uint16_t* q_pe;
   const uint16_t* kv;
+  const uint8_t* kv8;  // quantised cache (mla_decode_paged_fp8)
   const int32_t* block_table;
   const int32_t* seqlens;
   const int32_t* tile_meta;
@@ -158,6 +160,60 @@ struct TileLoad {
   __device__ __forceinline__ void issue(int i) const {
     const int r = i / kBlkCols, cb = i % kBlkCols;
     g2lds16_untracked(base, voff[r] + cb * 128, dst + r * kBlkRowStride + cb * kBlkBytes);
+  }
+};
+
+// Quantised cache tiles. A page is 64 rows of 640 bytes (512 e4m3 latent
+// codes, 64 bf16 key values) and then the 64 fp32 token scales. In LDS a
+// 32-token tile keeps the bf16 tile's image layout with 5 blocks of 128 bytes
+// per row (the same XOR permutation inside a block, block rows 5152 bytes
+// apart), followed by one copy of the page's 64 scales per wave.
+constexpr int kRowBytesF = MLA_FP8_ROW_BYTES;               // 640
+constexpr int kPageBytesF = MLA_FP8_PAGE_BYTES;             // 41216
+constexpr int kScalesOffF = MLA_FP8_SCALES_OFFSET;          // 40960
+constexpr int kBlkColsF = kRowBytesF / 128;                 // 5
+constexpr int kBlkRowStrideF = kBlkColsF * kBlkBytes + 32;  // 5152
+constexpr int kTileDataF = (kTile / 8) * kBlkRowStrideF;    // 20608
+constexpr int kTileStageBytesF = kTileDataF + 4 * 256;      // + 4 waves x 64 scales
+constexpr int kStagesF = 7;                                 // tile buffers in LDS (6 in flight)
+static_assert(kPage * kRowBytes >= kPageBytesF, "the zero page stands in for a quantised page too");
+
+__device__ __forceinline__ int lds_off_f(int r, int c) {
+  return (r >> 3) * kBlkRowStrideF + (c >> 3) * kBlkBytes + (r & 7) * 128 + (((c & 7) ^ chunk_swz(r & 7)) << 4);
+}
+
+// Loader of one quantised tile for the four waves of mla_decode_tsplit_kernel:
+// wave w copies block row w (8 tokens, 5 wave instructions of 1 KB) and the
+// page's 64 scales into its own 256-byte copy (one 4-byte load per lane), so
+// every wave's own loads cover the scales it reads. Rows past the cache length
+// repeat the page's last cached row; page ids outside the cache or past the
+// block table read the zero page and set the device error word.
+struct TileLoadF {
+  static constexpr int kInstr = kBlkColsF + 1;
+  const char* base;
+  unsigned voff;  // this lane's 16-byte slot in the wave's block row
+  unsigned dst;   // LDS byte address of the wave's block row
+  unsigned sdst;  // LDS byte address of the wave's scale copy
+  unsigned soff;  // this lane's scale
+
+  __device__ __forceinline__ void setup(const DecodeParams& P, int page, int half, int L, int pid,
+                                        MLA_LDS char* stage, int wave, int lane) {
+    const bool in_table = page < P.max_blocks;
+    const bool ok = in_table && pid >= 0 && pid < P.num_pages;
+    if (!ok) flag_error(in_table ? MLA_DEVERR_PAGE_ID : MLA_DEVERR_SEQ_TOO_LONG);
+    base = ok ? reinterpret_cast<const char*>(P.kv8) + (long long)pid * kPageBytesF
+              : reinterpret_cast<const char*>(g_zero_page);
+    const int last = ok ? min(kPage, L - page * kPage) - 1 : kPage - 1;
+    const int lr = lane >> 3, lc = (lane & 7) ^ chunk_swz(lane >> 3);
+    const int row = half * kTile + wave * 8 + lr;
+    voff = (unsigned)(min(row, last) * kRowBytesF + lc * 16);
+    dst = (unsigned)(uintptr_t)(stage + wave * kBlkRowStrideF);
+    sdst = (unsigned)(uintptr_t)(stage + kTileDataF + wave * 256);
+    soff = (unsigned)(kScalesOffF + lane * 4);
+  }
+  __device__ __forceinline__ void issue(int i) const {
+    if (i < kBlkColsF) g2lds16_untracked(base, voff + i * 128, dst + i * kBlkBytes);
+    else g2lds4_untracked(base, soff, sdst);
   }
 };
 
@@ -566,9 +622,19 @@ void mla_decode_kernel(DecodeParams P) {
 // pipeline, the fixed softmax reference with restart and the epilogue
 // formats are those of mla_decode_kernel; the reference of a row is shared by
 // the two waves that score it (exchanged once per piece through LDS).
+// With kFp8 the cache is the quantised page format: tiles are half as large
+// (seven buffers, six tiles in flight), the K and V fragments of the latent
+// part are e4m3 codes widened to bf16 in registers (exactly), each token's
+// scale multiplies its latent dot product before the positional part is added,
+// and the probabilities that weight its latent row carry the scale too. With
+// power-of-two scales this is, rounding step for rounding step, the bf16
+// kernel on the dequantised cache.
+template <bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_tsplit_kernel(DecodeParams P) {
-  __shared__ __attribute__((aligned(16))) char smem[kStages * kTileStageBytes];
+  constexpr int kStg = kFp8 ? kStagesF : kStages;
+  constexpr int kStgBytes = kFp8 ? kTileStageBytesF : kTileStageBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kStg * kStgBytes];
   __shared__ __attribute__((aligned(16))) char pbuf[2 * 32 * 32];  // P^T: [k-step][row][16 tokens] bf16 (permuted)
   __shared__ float xmax[4][16];  // per-wave row maxima (reference and restart exchanges)
   __shared__ float xl[4][16];    // per-wave row sums
@@ -588,8 +654,10 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
   const int split_begin = ldc(meta + 4);
   if (b_end < b_begin) return;
   const int M = P.M;
-  constexpr int kNLd = TileLoad<4>::kInstr;  // 9 loads per wave per tile
-  constexpr int kAhead = 3;
+  using Loader = std::conditional_t<kFp8, TileLoadF, TileLoad<4>>;
+  constexpr int kNLd = Loader::kInstr;       // loads per wave per tile: 9 (bf16) or 6 (quantised)
+  constexpr int kAhead = kFp8 ? 6 : 3;       // tiles in flight
+  static_assert((kAhead - 1) * kNLd < 64 && kAhead < kStg, "load pipeline depth");
   constexpr int kSlots = 18 + 8;             // matrix instructions per tile and wave
 
   // K fragment (A operand) of k-step ks: token 16 th + l % 16 of the tile,
@@ -601,6 +669,20 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
     for (int p = 0; p < 2; ++p)
       ka[p] = (r >> 3) * kBlkRowStride + lr * 128 + (((4 * p + (lane >> 4)) ^ chunk_swz(lr)) << 4);
   }
+  // Quantised tiles: the latent fragment of k-step ks (< 16) is 8 codes of
+  // token 16 th + l % 16 at row byte 32 ks + 8 (l / 16): 16-byte chunk
+  // 2 ks + l / 32, half (l / 16) % 2 -> kl[ks % 4] + (ks / 4) * 1024. The
+  // positional fragments (k-steps 16, 17) are bf16 in the row's fifth block.
+  int kl[4], kp[2];
+  if constexpr (kFp8) {
+    const int r = 16 * th + (lane & 15), lr = r & 7, lg = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      kl[q] = (r >> 3) * kBlkRowStrideF + lr * 128 + (((2 * q + (lg >> 1)) ^ chunk_swz(lr)) << 4) + 8 * (lg & 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      kp[p] = (r >> 3) * kBlkRowStrideF + 4 * kBlkBytes + lr * 128 + (((4 * p + lg) ^ chunk_swz(lr)) << 4);
+  }
   // V^T fragment of this wave's d-tile dt (global d-tile 4 wave + dt) and k-step kk:
   //   v_base[dt % 2] + (2 wave + dt / 2) * 1024 + 2 kk * kBlkRowStride (+ kBlkRowStride)
   int v_base[2];
@@ -611,6 +693,23 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
     for (int p2 = 0; p2 < 2; ++p2)
       v_base[p2] = lr * 128 + (((4 * p2 + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1)) ^ chunk_swz(lr)) << 4) +
                    8 * (j16 & 1) + wave * 2048;
+  }
+  // Quantised tiles: V^T fragment of d-tile dt (d = 128 wave + 32 dt + l % 32)
+  // and k-step kk by one 8-bit transposed read. Its 8 tokens must be those of
+  // the bf16 fragment, in the same order (the k order P^T is stored in): lane
+  // group g = l / 32 holds tokens 16 kk + 4 g + {0, 1, 2, 3, 8, 9, 10, 11}. The
+  // k-th byte a lane receives comes from the row that lanes 2 k and 2 k + 1 of
+  // its 16-lane block B address, so lane j of block B addresses token
+  // 16 kk + 4 (B / 2) + (j / 2) % 4 + 8 (j / 8) at row byte
+  // 128 wave + 32 dt + 16 (B % 2) + 8 (j % 2)  ->  vf[dt] + 2 kk * kBlkRowStrideF
+  int vf[4];
+  if constexpr (kFp8) {
+    const int B = lane >> 4, j = lane & 15;
+    const int lr = 4 * (B >> 1) + ((j >> 1) & 3);  // token within its 8-token block row
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      vf[dt] = (j >> 3) * kBlkRowStrideF + wave * kBlkBytes + lr * 128 +
+               (((2 * dt + (B & 1)) ^ chunk_swz(lr)) << 4) + 8 * (j & 1);
   }
 
   for (int b = b_begin; b <= b_end; ++b) {
@@ -646,13 +745,13 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
 
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     f32x16 acc[4];
-    TileLoad<4> ld;
+    Loader ld;
     int pid = -1;
     auto issue_first_tiles = [&]() {
 #pragma unroll 1
       for (int t = 0; t < min(kAhead, n_tiles); ++t) {
         if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
-        ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
+        ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStg) * kStgBytes, wave, lane);
 #pragma unroll
         for (int i = 0; i < kNLd; ++i) ld.issue(i);
       }
@@ -666,25 +765,59 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
       m_ref = m_seen;
       l_run = 0.f;
       for (int j = 0; j < n_tiles; ++j) {
-        const int later = min(kAhead - 1, n_tiles - 1 - j);
-        if (later >= 2) wait_vmcnt<2 * kNLd>();
-        else if (later == 1) wait_vmcnt<kNLd>();
-        else wait_vmcnt<0>();
+        const int later = min(kAhead - 1, n_tiles - 1 - j);  // this wave's later tiles still loading
+        switch (later) {  // uniform
+          case 5: wait_vmcnt<(kAhead > 5 ? 5 * kNLd : 0)>(); break;
+          case 4: wait_vmcnt<(kAhead > 4 ? 4 * kNLd : 0)>(); break;
+          case 3: wait_vmcnt<(kAhead > 3 ? 3 * kNLd : 0)>(); break;
+          case 2: wait_vmcnt<2 * kNLd>(); break;
+          case 1: wait_vmcnt<kNLd>(); break;
+          default: wait_vmcnt<0>(); break;
+        }
         barrier_keep_loads();
         const bool more = j + kAhead < n_tiles;
         if (more) {
           const int t = j + kAhead;
           if ((t & 1) == 0) pid = fetch_pid(P, b, p_lo + (t >> 1));
-          ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStages) * kTileStageBytes, wave, lane);
+          ld.setup(P, p_lo + (t >> 1), t & 1, L, pid, lds + (t % kStg) * kStgBytes, wave, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
-        MLA_LDS char* tile = lds + (j % kStages) * kTileStageBytes;
+        MLA_LDS char* tile = lds + (j % kStg) * kStgBytes;
 #define MLA_TS_LOAD_SLOT(m) \
   if ((((m) + 1) * kNLd) / kSlots != ((m) * kNLd) / kSlots && more) ld.issue(((m) * kNLd) / kSlots);
 
         // ---- S^T = K Q^T for 16 tokens x 16 rows, 576 deep ----
         f32x4 sc = f32x4{};
-        {
+        f32x4 tsc;  // quantised tiles: the scales of this lane's 4 tokens
+        if constexpr (kFp8) {
+          // codes read four k-steps ahead, widened one k-step ahead (under the
+          // running matrix instruction)
+          u32x2 kr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kr[i] = lds_read8(tile, kl[i]);
+          bf16x8 kb = fp8x8_to_bf16(kr[0]);
+#pragma unroll
+          for (int ks = 0; ks < 16; ++ks) {
+            const bf16x8 cur = kb;
+            sc = mfma16(cur, qf[ks], sc);
+            if (ks + 1 < 16) kb = fp8x8_to_bf16(kr[(ks + 1) & 3]);
+            if (ks + 4 < 16) kr[ks & 3] = lds_read8(tile, kl[(ks + 4) & 3] + ((ks + 4) >> 2) * kBlkBytes);
+            MLA_TS_LOAD_SLOT(ks)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // the latent dot products carry each token's scale; then the positional part
+          tsc = *reinterpret_cast<const MLA_LDS f32x4*>(tile + kTileDataF + wave * 256 +
+                                                        ((j & 1) * kTile + 16 * th + 4 * (lane >> 4)) * 4);
+          const bf16x8 r0 = lds_read16(tile, kp[0]), r1 = lds_read16(tile, kp[1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[i] *= tsc[i];
+          sc = mfma16(r0, qf[16], sc);
+          MLA_TS_LOAD_SLOT(16)
+          __builtin_amdgcn_sched_barrier(0);
+          sc = mfma16(r1, qf[17], sc);
+          MLA_TS_LOAD_SLOT(17)
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
           bf16x8 kr[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) kr[i] = lds_read16(tile, ka[i & 1] + (i >> 1) * kBlkBytes);
@@ -722,7 +855,10 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
         for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(sc[i] * P.scale_log2e - msub);
           l_run += p;
-          pw[i] = (__bf16)p;
+          // quantised tiles: the weight of the token's latent row carries its
+          // scale (a masked token weighs 0 whatever its scale slot holds)
+          if constexpr (kFp8) pw[i] = (__bf16)(p > 0.f ? p * tsc[i] : 0.f);
+          else pw[i] = (__bf16)p;
         }
         // P^T of k-step th, row 16 rh + l % 16, stored in the k order of the
         // V^T fragments (lane group g of a fragment holds tokens 4 g .. 4 g + 3
@@ -733,7 +869,24 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
         barrier_keep_loads();
 
         // ---- O^T += V^T P^T: this wave's 128 columns, all 32 rows, 32 tokens ----
-        {
+        if constexpr (kFp8) {
+          bf16x8 pf[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) pf[kk] = lds_read16(pb, kk * 1024 + (lane & 31) * 32 + (lane >> 5) * 16);
+          u32x2 vq[8];
+#pragma unroll
+          for (int it = 0; it < 8; ++it) vq[it] = lds_read_tr8(tile, vf[it >> 1] + 2 * (it & 1) * kBlkRowStrideF);
+          bf16x8 vb = fp8x8_to_bf16(vq[0]);
+#pragma unroll
+          for (int it = 0; it < 8; ++it) {  // it = dt * 2 + kk; widened one step ahead
+            const int dt = it >> 1, kk = it & 1;
+            const bf16x8 cur = vb;
+            acc[dt] = mfma32(cur, pf[kk], acc[dt]);
+            if (it + 1 < 8) vb = fp8x8_to_bf16(vq[it + 1]);
+            MLA_TS_LOAD_SLOT(18 + it)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
           bf16x8 pf[2];
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) pf[kk] = lds_read16(pb, kk * 1024 + (lane & 31) * 32 + (lane >> 5) * 16);
@@ -1052,6 +1205,85 @@ __global__ __launch_bounds__(64) void mla_append_kernel(const uint16_t* new_rows
   if (lane + 64 < kChunks) dst[lane + 64] = v1;
 }
 
+// Scale exponent of a quantised row: the smallest e with amax <= 448 * 2^e,
+// at least -126 (0 for an all-zero row), from the bits of amax: with
+// amax = m * 2^E, m in [1, 2), e = E - 8, one more when m > 1.75.
+__device__ __forceinline__ int fp8_scale_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const unsigned bits = __builtin_bit_cast(unsigned, amax);
+  const int biased = (int)((bits >> 23) & 0xFF);
+  if (biased == 0) return -126;  // below 2^-126 the floor applies
+  const int e = biased - 127 - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return max(-126, e);
+}
+
+// One wave quantises one cache row: lane l takes latent values 8 l .. 8 l + 7;
+// the wave's max |value| gives the scale 2^e; each value is divided by it
+// (exact) and rounded to the nearest e4m3 code (ties to even; the values then
+// lie within +-448). Lanes 0..15 copy the 64 bf16 key values, lane 0 writes
+// the scale.
+__device__ __forceinline__ void quantize_row_wave(const uint16_t* src, uint8_t* row, float* scale_slot, int lane) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * lane);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+    x[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const int e = fp8_scale_exponent(amax);
+  u32x2 out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const unsigned lo =
+        (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * w], -e), ldexpf(x[4 * w + 1], -e), 0, false) & 0xFFFFu;
+    const unsigned hi =
+        (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * w + 2], -e), ldexpf(x[4 * w + 3], -e), 0, false) & 0xFFFFu;
+    out[w] = lo | (hi << 16);
+  }
+  *reinterpret_cast<u32x2*>(row + 8 * lane) = out;
+  if (lane < 16) *reinterpret_cast<u32x2*>(row + kDLat + 8 * lane) = *reinterpret_cast<const u32x2*>(src + kDLat + 4 * lane);
+  if (lane == 0) *scale_slot = ldexpf(1.0f, e);
+}
+
+// Whole-cache quantisation: one wave per row, 16 workgroups of 4 rows per page.
+__global__ __launch_bounds__(256) void mla_quantize_pages_kernel(const uint16_t* kv, uint8_t* kv8) {
+  const long long page = blockIdx.x / 16;
+  const int row = (blockIdx.x % 16) * 4 + (threadIdx.x >> 6);
+  uint8_t* dst = kv8 + page * kPageBytesF;
+  quantize_row_wave(kv + (page * kPage + row) * kDRow, dst + row * kRowBytesF,
+                    reinterpret_cast<float*>(dst + kScalesOffF) + row, threadIdx.x & 63);
+}
+
+// Quantise-on-append: one wave per new row, the checks of mla_append_kernel.
+__global__ __launch_bounds__(64) void mla_append_fp8_kernel(const uint16_t* new_rows, uint8_t* kv8,
+                                                            long long num_pages, const int32_t* block_table,
+                                                            int max_blocks, const int32_t* seqlens, int s_q) {
+  const int b = blockIdx.x / s_q, j = blockIdx.x % s_q;
+  const int t = seqlens[b] - s_q + j;  // token index of this new row
+  if (t < 0) {
+    if (threadIdx.x == 0) flag_error(MLA_DEVERR_SHORT_SEQ);
+    return;
+  }
+  const int page = t / kPage;
+  if (page >= max_blocks) {
+    if (threadIdx.x == 0) flag_error(MLA_DEVERR_SEQ_TOO_LONG);
+    return;
+  }
+  const int pid = block_table[(long long)b * max_blocks + page];
+  if (pid < 0 || pid >= num_pages) {
+    if (threadIdx.x == 0) flag_error(MLA_DEVERR_PAGE_ID);
+    return;
+  }
+  uint8_t* dst = kv8 + (long long)pid * kPageBytesF;
+  quantize_row_wave(new_rows + ((long long)b * s_q + j) * kDRow, dst + (t % kPage) * kRowBytesF,
+                    reinterpret_cast<float*>(dst + kScalesOffF) + (t % kPage), threadIdx.x);
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -1109,7 +1341,8 @@ static int check_decode_args(const char* fn, const uint16_t* q_lat, const uint16
 // Launches of one decode call (arguments already checked; `ws` holds at least
 // mla_workspace_bytes(b, s_q, h, num_slots) bytes, 256-byte aligned).
 static int decode_launch(const char* fn, const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
-                         const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table, int max_blocks,
+                         const uint16_t* kv_cache, const uint8_t* kv8, int64_t num_pages,
+                         const int32_t* block_table, int max_blocks,
                          const int32_t* cache_seqlens, int b, int s_q, int h, float softmax_scale, int causal,
                          const int32_t* tile_meta, const int32_t* num_splits, int num_slots, char* ws,
                          uint16_t* o_lat, float* lse, void* stream) {
@@ -1122,6 +1355,7 @@ static int decode_launch(const char* fn, const uint16_t* q_lat, const uint16_t* 
   P.q_lat_lo = q_lat_lo;
   P.q_pe = q_pe;
   P.kv = kv_cache;
+  P.kv8 = kv8;
   P.block_table = block_table;
   P.seqlens = cache_seqlens;
   P.tile_meta = tile_meta;
@@ -1147,7 +1381,10 @@ static int decode_launch(const char* fn, const uint16_t* q_lat, const uint16_t* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int grid = R == 1 ? num_slots : ((num_slots + 7) / 8) * 8 * R;
   switch (nw) {
-    case 1: hipLaunchKernelGGL(mla_decode_tsplit_kernel, dim3(grid), dim3(256), 0, st, P); break;
+    case 1:
+      if (kv8) hipLaunchKernelGGL(mla_decode_tsplit_kernel<true>, dim3(grid), dim3(256), 0, st, P);
+      else hipLaunchKernelGGL(mla_decode_tsplit_kernel<false>, dim3(grid), dim3(256), 0, st, P);
+      break;
     case 2: hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(grid), dim3(128), 0, st, P); break;
     default: hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(grid), dim3(256), 0, st, P); break;
   }
@@ -1182,8 +1419,8 @@ extern "C" int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo,
   const size_t need = mla_workspace_bytes(b, s_q, h, num_slots);
   if (workspace_bytes < need)
     return set_error(MLA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
-  return decode_launch(fn, q_lat, q_lat_lo, q_pe, kv_cache, num_pages, block_table, max_blocks, cache_seqlens, b,
-                       s_q, h, softmax_scale, causal, tile_meta, num_splits, num_slots,
+  return decode_launch(fn, q_lat, q_lat_lo, q_pe, kv_cache, nullptr, num_pages, block_table, max_blocks,
+                       cache_seqlens, b, s_q, h, softmax_scale, causal, tile_meta, num_splits, num_slots,
                        static_cast<char*>(workspace), o_lat, lse, stream);
 }
 
@@ -1241,8 +1478,9 @@ extern "C" int mla_decode_paged_noalloc(const uint16_t* q_lat, const uint16_t* q
                      fn, need, b, s_q, h, num_slots, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
   char* ws = nullptr;
   if (int rc = scratch_for_current_device(fn, &ws)) return rc;
-  return decode_launch(fn, q_lat, q_lat_lo, q_pe, kv_cache, num_pages, block_table, max_blocks, cache_seqlens, b,
-                       s_q, h, softmax_scale, causal, tile_meta, num_splits, num_slots, ws, o_lat, lse, stream);
+  return decode_launch(fn, q_lat, q_lat_lo, q_pe, kv_cache, nullptr, num_pages, block_table, max_blocks,
+                       cache_seqlens, b, s_q, h, softmax_scale, causal, tile_meta, num_splits, num_slots, ws, o_lat,
+                       lse, stream);
 }
 
 extern "C" int mla_gather_pages(const uint16_t* kv_cache, int64_t num_pages, const int32_t* block_table,
@@ -1298,5 +1536,63 @@ extern "C" int mla_take_device_error(int* bits) {
       hipMemcpyToSymbol(HIP_SYMBOL(g_device_error), &zero, sizeof(int), 0, hipMemcpyHostToDevice) != hipSuccess)
     return set_error(MLA_ERR_HIP, "mla_take_device_error: cannot read the device error word");
   *bits = v;
+  return clear_error();
+}
+
+extern "C" int mla_decode_paged_fp8(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,
+                                    const uint8_t* kv_fp8, int64_t num_pages, const int32_t* block_table,
+                                    int max_blocks, const int32_t* cache_seqlens, int b, int s_q, int h,
+                                    float softmax_scale, int causal, const int32_t* tile_meta,
+                                    const int32_t* num_splits, int num_slots, void* workspace,
+                                    size_t workspace_bytes, uint16_t* o_lat, float* lse, void* stream) {
+  const char* fn = "mla_decode_paged_fp8";
+  if (!workspace) return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+  if (int rc = check_decode_args(fn, q_lat, q_lat_lo, q_pe, reinterpret_cast<const uint16_t*>(kv_fp8), num_pages,
+                                 block_table, max_blocks, cache_seqlens, b, s_q, h, softmax_scale, tile_meta,
+                                 num_splits, num_slots, o_lat, lse))
+    return rc;
+  if (s_q * h > 32)
+    return set_error(MLA_ERR_UNSUPPORTED, "%s: built for at most 32 query rows per sequence (s_q * h = %d)", fn,
+                     s_q * h);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = mla_workspace_bytes(b, s_q, h, num_slots);
+  if (workspace_bytes < need)
+    return set_error(MLA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  return decode_launch(fn, q_lat, q_lat_lo, q_pe, nullptr, kv_fp8, num_pages, block_table, max_blocks, cache_seqlens,
+                       b, s_q, h, softmax_scale, causal, tile_meta, num_splits, num_slots,
+                       static_cast<char*>(workspace), o_lat, lse, stream);
+}
+
+extern "C" int mla_quantize_pages(const uint16_t* kv_cache, int64_t num_pages, uint8_t* kv_fp8, void* stream) {
+  const char* fn = "mla_quantize_pages";
+  if (!kv_cache || !kv_fp8) return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+  if (num_pages < 1 || num_pages > (1LL << 26))
+    return set_error(MLA_ERR_INVALID_ARG, "%s: num_pages must be in [1, 2^26] (got %lld)", fn, (long long)num_pages);
+  if (reinterpret_cast<uintptr_t>(kv_cache) % 16 || reinterpret_cast<uintptr_t>(kv_fp8) % 16)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: kv_cache and kv_fp8 must be 16-byte aligned", fn);
+  hipLaunchKernelGGL(mla_quantize_pages_kernel, dim3((unsigned)(num_pages * 16)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), kv_cache, kv_fp8);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess)
+    return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return clear_error();
+}
+
+extern "C" int mla_append_kv_fp8(const uint16_t* new_rows, uint8_t* kv_fp8, int64_t num_pages,
+                                 const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int b,
+                                 int s_q, void* stream) {
+  const char* fn = "mla_append_kv_fp8";
+  if (!new_rows || !kv_fp8 || !block_table || !cache_seqlens)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+  if (b < 1) return set_error(MLA_ERR_INVALID_ARG, "%s: b must be >= 1 (got %d)", fn, b);
+  if (s_q < 1 || s_q > 8) return set_error(MLA_ERR_INVALID_ARG, "%s: s_q must be in [1, 8] (got %d)", fn, s_q);
+  if (num_pages < 1 || max_blocks < 1)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: num_pages and max_blocks must be >= 1", fn);
+  if (reinterpret_cast<uintptr_t>(new_rows) % 16 || reinterpret_cast<uintptr_t>(kv_fp8) % 16)
+    return set_error(MLA_ERR_INVALID_ARG, "%s: new_rows and kv_fp8 must be 16-byte aligned", fn);
+  hipLaunchKernelGGL(mla_append_fp8_kernel, dim3(b * s_q), dim3(64), 0, static_cast<hipStream_t>(stream), new_rows,
+                     kv_fp8, (long long)num_pages, block_table, max_blocks, cache_seqlens, s_q);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess)
+    return set_error(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return clear_error();
 }

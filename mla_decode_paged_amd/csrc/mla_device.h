@@ -96,7 +96,46 @@ __device__ __forceinline__ void g2lds16_untracked(const char* base, unsigned vof
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
 }
 
+// The same for 4 bytes per lane (lane l's bytes land at lds_addr + 4 * lane).
+__device__ __forceinline__ void g2lds4_untracked(const char* base, unsigned voff, unsigned lds_addr) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Eight fp8 e4m3 codes (bytes 0..7 of v) -> eight bf16 values in the same
+// order, exactly (every e4m3 value is a bf16 value). Written as the
+// instruction itself: lane layouts of the conversion builtins' second result
+// were not what the hardware returns, while this form was checked on all 256
+// codes. The two trailing wait states cover a matrix instruction that reads
+// the result next (the compiler does not see the writes inside the asm).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 v) {
+  unsigned a, b, c, d;
+  asm("v_cvt_scalef32_pk_bf16_fp8 %0, %4, 1.0\n\t"
+      "v_cvt_scalef32_pk_bf16_fp8 %1, %4, 1.0 op_sel:[1,0,0]\n\t"
+      "v_cvt_scalef32_pk_bf16_fp8 %2, %5, 1.0\n\t"
+      "v_cvt_scalef32_pk_bf16_fp8 %3, %5, 1.0 op_sel:[1,0,0]\n\t"
+      "s_nop 1"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"(v[0]), "v"(v[1]));
+  return as_bf16x8(u32x4{a, b, c, d});
+}
+
+// 8-byte LDS read.
+__device__ __forceinline__ u32x2 lds_read8(const MLA_LDS char* base, int byte_off) {
+  return *reinterpret_cast<const MLA_LDS u32x2*>(base + byte_off);
+}
+
+// Transposed 8-bit LDS read (ds_read_b64_tr_b8): within each 16-lane block,
+// lane j supplies the address of 8 consecutive bytes of row r0 + j / 2 at
+// byte column c0 + 8 (j % 2); lane i receives byte column c0 + i of rows
+// r0 .. r0 + 7 (checked on the hardware for all 64 lanes).
+__device__ __forceinline__ u32x2 lds_read_tr8(const MLA_LDS char* base, int byte_off) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      reinterpret_cast<MLA_LDS i32x2*>(const_cast<MLA_LDS char*>(base) + byte_off));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -171,3 +171,32 @@ def test_noalloc_scratch_size_matches_the_header(lib):
     for b, s_q, h, slots in [(128, 1, 32, 256), (128, 1, 128, 256), (16, 1, 128, 256), (128, 2, 128, 128),
                              (32, 8, 128, 32)]:
         assert lib.mla_workspace_bytes(b, s_q, h, slots) <= mla.NOALLOC_SCRATCH_BYTES
+
+
+def test_quantised_cache_calls_reject(lib):
+    """The quantised-cache entry points check their arguments before anything is launched."""
+    assert lib.mla_quantize_pages(None, 4, FAKE, None) == INVALID
+    assert lib.mla_quantize_pages(FAKE, 0, FAKE, None) == INVALID
+    assert lib.mla_quantize_pages(FAKE, 4, ctypes.c_void_p((1 << 20) + 8), None) == INVALID
+    assert lib.mla_append_kv_fp8(FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 9, None) == INVALID
+    assert lib.mla_append_kv_fp8(FAKE, None, 4, FAKE, 4, FAKE, 2, 1, None) == INVALID
+    assert lib.mla_append_kv_fp8(FAKE, ctypes.c_void_p((1 << 20) + 4), 4, FAKE, 4, FAKE, 2, 1, None) == INVALID
+    args = [FAKE, None, FAKE, FAKE, 10, FAKE, 4, FAKE, 2, 1, 64, 0.07, 0, FAKE, FAKE, 8, FAKE, 1 << 30, FAKE, FAKE,
+            None]
+    assert lib.mla_decode_paged_fp8(*args) == UNSUPPORTED  # 64 rows: more than the 32 it is built for
+    assert "at most 32 query rows" in lib.mla_last_error().decode()
+    args[10] = 32
+    args[16] = None
+    assert lib.mla_decode_paged_fp8(*args) == INVALID      # no workspace
+    args[16] = FAKE
+    args[17] = 1000
+    assert lib.mla_decode_paged_fp8(*args) == WORKSPACE
+
+
+def test_quantised_page_constants():
+    import mla_decode_paged_amd as mla
+    text = open(HEADER).read()
+    assert "#define MLA_FP8_ROW_BYTES 640" in text
+    assert mla.FP8_ROW_BYTES == 640 and mla.FP8_PAGE_BYTES == 64 * 640 + 256 == 41216
+    from oracle import kv_quant
+    assert kv_quant.PAGE_BYTES == mla.FP8_PAGE_BYTES and kv_quant.ROW_BYTES == mla.FP8_ROW_BYTES
