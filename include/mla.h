@@ -94,7 +94,8 @@ int mla_num_slots(int b, int s_q, int h, int* num_slots /* host out */);
 /* Bytes of workspace mla_decode_paged needs for this shape and slot count:
  * partial rows of split sequences as fp16 [b + num_slots, M, 512] (each row
  * divided by its largest magnitude), their lse and row scales, fp32
- * [b + num_slots, M] each. Returns 0 on bad arguments. Host query. */
+ * [b + num_slots, M] each. Returns 0 for a shape the decode does not accept.
+ * Host query. */
 size_t mla_workspace_bytes(int b, int s_q, int h, int num_slots);
 
 /* mla_get_metadata - split-KV work plan (FlashMLA usage: planned once per
@@ -103,7 +104,7 @@ size_t mla_workspace_bytes(int b, int s_q, int h, int num_slots);
  * cache_seqlens  int32 [b]         cache length L_b of each sequence, counting
  *                                  the s_q new tokens; L_b <= 0 is empty.
  * b              1..MLA_MAX_BATCH
- * num_slots      >= 1, the grid mla_decode_paged will run (mla_num_slots)
+ * num_slots      1..2^20, the grid mla_decode_paged will run (mla_num_slots)
  * split_overhead >= 0, fixed cost of one sequence piece, in pages
  * tile_meta      int32 [num_slots, 8] out
  * num_splits     int32 [b + 1] out: prefix sums of the pieces per sequence
@@ -174,8 +175,8 @@ int mla_absorb_q_with_plan(const uint16_t* q_nope, const uint16_t* w_uk, uint16_
  *                  256-byte aligned; contents need not be initialised
  * o_lat            bf16 [b, s_q, h, 512] out
  * lse              fp32 [b, s_q, h] out
- * softmax_scale > 0 (1/sqrt(192) for DeepSeek-V3), b >= 1, 1 <= s_q <= 8,
- * h in {16, 32, 64, 128}, num_pages >= 1.
+ * softmax_scale > 0 (1/sqrt(192) for DeepSeek-V3), 1 <= b <= MLA_MAX_BATCH,
+ * 1 <= s_q <= 8, h in {16, 32, 64, 128}, num_pages >= 1, num_slots 1..2^20.
  * Page ids and lengths that break the contract are read as zero rows and set
  * a device error bit (mla_take_device_error). */
 int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_lat_lo, const uint16_t* q_pe,

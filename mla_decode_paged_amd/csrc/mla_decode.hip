@@ -1308,9 +1308,13 @@ extern "C" int mla_num_slots(int b, int s_q, int h, int* num_slots) {
 // and fp32 row scales [splits, M], each region 256-byte aligned
 // (splits = b + num_slots bounds the plan's pieces).
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+constexpr int kMaxSlots = 1 << 20;  // far beyond any useful grid
 
 extern "C" size_t mla_workspace_bytes(int b, int s_q, int h, int num_slots) {
-  if (b < 1 || s_q < 1 || h < 1 || num_slots < 1) return 0;
+  // only shapes the decode accepts: the size below then cannot overflow
+  if (b < 1 || b > MLA_MAX_BATCH || s_q < 1 || s_q > 8 || (h != 16 && h != 32 && h != 64 && h != 128) ||
+      num_slots < 1 || num_slots > kMaxSlots)
+    return 0;
   const size_t M = (size_t)s_q * h;
   const size_t splits = (size_t)b + num_slots;
   return round256(splits * M * kDLat * 2) + 2 * round256(splits * M * sizeof(float));
@@ -1326,8 +1330,10 @@ static int check_decode_args(const char* fn, const uint16_t* q_lat, const uint16
       !lse)
     return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
   if (int rc = check_shape(fn, b, s_q, h)) return rc;
+  if (b > MLA_MAX_BATCH) return set_error(MLA_ERR_INVALID_ARG, "%s: b must be <= %d (got %d)", fn, MLA_MAX_BATCH, b);
   if (num_pages < 1 || max_blocks < 1 || num_slots < 1)
     return set_error(MLA_ERR_INVALID_ARG, "%s: num_pages, max_blocks and num_slots must be >= 1", fn);
+  if (num_slots > kMaxSlots) return set_error(MLA_ERR_INVALID_ARG, "%s: num_slots must be <= %d", fn, kMaxSlots);
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return set_error(MLA_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", fn);
   for (const void* p : {(const void*)q_lat, (const void*)q_pe, (const void*)kv_cache, (const void*)o_lat})

@@ -141,7 +141,8 @@ inline int check_plan_args(const char* fn, const int32_t* cache_seqlens, int b, 
     return set_error(MLA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
   if (b < 1 || b > MLA_MAX_BATCH)
     return set_error(MLA_ERR_INVALID_ARG, "%s: b must be in [1, %d] (got %d)", fn, MLA_MAX_BATCH, b);
-  if (num_slots < 1) return set_error(MLA_ERR_INVALID_ARG, "%s: num_slots must be >= 1", fn);
+  if (num_slots < 1 || num_slots > (1 << 20))
+    return set_error(MLA_ERR_INVALID_ARG, "%s: num_slots must be in [1, 2^20] (got %d)", fn, num_slots);
   if (split_overhead < 0) return set_error(MLA_ERR_INVALID_ARG, "%s: split_overhead must be >= 0", fn);
   return MLA_OK;
 }
