@@ -14,7 +14,9 @@ from a HIP graph (one graph per rotating input set, recorded through torch's
 graph capture on the library's stream), so no host launch gap sits between the
 kernels of a step. Before the timed steps, untimed steps run for
 --warmup-seconds (the clock settles only under sustained load; reported as
-`warmup_s`) and then --warmup steps. `eager_us_per_step` is at least 50 of the
+`warmup_s`) and then --warmup steps; the graph replays get the same time-based
+warm-up after capture (`graph_warmup_replays`), since the GPU idles while the
+graphs are recorded. `eager_us_per_step` is at least 50 of the
 same steps launched eagerly; hipEvents around each call give the medians in
 `stage_us` and the decode call's `decode_us` and roofline. With the default
 workload (full_heads) the matrix-bound multi_token workload is measured in the
@@ -192,7 +194,8 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float, kv: str = 
     """One workload: R rotating input sets resident in HBM; a time-based warm-up (the clock settles only
     after about 100 steps of load), then ``warmup`` untimed steps; max(steps, 50) eager steps with
     hipEvents around every call (their medians give the per-call times); then the same steps captured
-    in HIP graphs, ``warmup`` untimed replays and exactly ``steps`` timed replays (the step time)."""
+    in HIP graphs, replayed untimed for ``warmup_s`` seconds (the clock falls while the graphs are
+    recorded) and ``warmup`` more times, then exactly ``steps`` timed replays (the step time)."""
     import numpy as np
     import torch
 
@@ -275,6 +278,7 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float, kv: str = 
     # each step's launches are recorded once, so a replay has no host launch
     # gaps between its kernels.
     us_step_graph = None
+    n_graph_warm = 0
     if not args.no_graph:
         graphs = []
         for r in range(R):
@@ -282,6 +286,17 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float, kv: str = 
             with torch.cuda.graph(g):
                 step(r, False)
             graphs.append(g)
+        # The GPU idles while the graphs are recorded and its clock drops: the
+        # first ~100 replays after capture run about 15 % slower. The replays
+        # get the same time-based warm-up as the eager steps, then the
+        # requested warm-up replays, before exactly `steps` timed replays.
+        t0 = time.perf_counter()
+        n_graph_warm = 0
+        while time.perf_counter() - t0 < warmup_s:
+            for _ in range(25):
+                graphs[n_graph_warm % R].replay()
+                n_graph_warm += 1
+            torch.cuda.synchronize()
         for i in range(max(warmup, R)):
             graphs[i % R].replay()
         torch.cuda.synchronize()
@@ -293,7 +308,7 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float, kv: str = 
         assert mla.take_device_error() == 0
         del graphs
     out = dict(sets=sets, R=R, slots=slots, us_step_eager=us_step_eager, us_step_graph=us_step_graph,
-               n_ev=n_ev, t_warm=t_warm, n_time_warm=n_time_warm,
+               n_ev=n_ev, t_warm=t_warm, n_time_warm=n_time_warm, n_graph_warm=n_graph_warm,
                median={k: float(np.median(v)) for k, v in per_call.items()},
                mean={k: float(np.mean(v)) for k, v in per_call.items()})
     return out
@@ -330,6 +345,7 @@ def summary(inp, m, traffic, seed, kv="bf16"):
         "roofline": roofline_entry(work, t_dec, traffic),
         "num_slots": m["slots"], "rotating_copies": m["R"],
         "warmup_s": round(m["t_warm"], 3), "warmup_time_steps": m["n_time_warm"],
+        "graph_warmup_replays": m["n_graph_warm"],
     }
 
 
@@ -404,7 +420,8 @@ def main():
                    "rotating_copies": main_sum["rotating_copies"]},
     }
     for k in ("step_mode", "eager_us_per_step", "stage_us", "stage_us_mean", "timed_calls", "decode_us",
-              "latent_kv_TBps", "decode_TFLOPs", "hbm_frac", "mfma_frac", "roofline", "warmup_time_steps"):
+              "latent_kv_TBps", "decode_TFLOPs", "hbm_frac", "mfma_frac", "roofline", "warmup_time_steps",
+              "graph_warmup_replays"):
         line[k] = main_sum[k]
     line["append_kv"] = append
     for name in extra:
