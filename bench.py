@@ -9,10 +9,11 @@ synthetic tensors already resident in HBM. To keep the 256 MB Infinity Cache
 from serving repeats, R copies of every input and output rotate, with R times
 the working set above 1 GiB.
 
-`value` is the wall time per step over exactly --steps steps, each replayed
-from a HIP graph (one graph per rotating input set, recorded through torch's
-graph capture on the library's stream), so no host launch gap sits between the
-kernels of a step. Before the timed steps, untimed steps run for
+`value` is the wall time per step over exactly --steps steps replayed from HIP
+graphs recorded through torch's graph capture on the library's stream: one graph
+holds one step on each rotating input set (the graph launch cost spread over
+those steps, as over the layers of a model in one graph), single-step graphs
+cover the remainder, and no host launch gap sits between the kernels of a step. Before the timed steps, untimed steps run for
 --warmup-seconds (the clock settles only under sustained load; reported as
 `warmup_s`) and then --warmup steps; the graph replays get the same time-based
 warm-up after capture (`graph_warmup_replays`), since the GPU idles while the
@@ -194,8 +195,9 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float, kv: str = 
     """One workload: R rotating input sets resident in HBM; a time-based warm-up (the clock settles only
     after about 100 steps of load), then ``warmup`` untimed steps; max(steps, 50) eager steps with
     hipEvents around every call (their medians give the per-call times); then the same steps captured
-    in HIP graphs, replayed untimed for ``warmup_s`` seconds (the clock falls while the graphs are
-    recorded) and ``warmup`` more times, then exactly ``steps`` timed replays (the step time)."""
+    in a HIP graph of R steps (one per input set) and in single-step graphs, replayed untimed for
+    ``warmup_s`` seconds (the clock falls while the graphs are recorded) and ``warmup`` more steps,
+    then exactly ``steps`` timed steps (the step time)."""
     import numpy as np
     import torch
 
@@ -274,39 +276,50 @@ def measure(mla, inp, args, steps: int, warmup: int, warmup_s: float, kv: str = 
     us_step_eager = (time.perf_counter() - t0) / n_ev * 1e6
     assert mla.take_device_error() == 0
     per_call = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in ev.items()}
-    # The same steps replayed from HIP graphs, one per rotating input set:
-    # each step's launches are recorded once, so a replay has no host launch
-    # gaps between its kernels.
+    # The same steps replayed from HIP graphs: each step's launches are
+    # recorded once, so a replay has no host launch gaps between its kernels.
     us_step_graph = None
     n_graph_warm = 0
     if not args.no_graph:
-        graphs = []
+        # One graph holds one step on each of the R rotating input sets, so the
+        # launch cost of a graph is spread over R steps, as it is over the
+        # layers of a model captured in one graph; single-step graphs cover a
+        # step count that is not a multiple of R. Each step is the whole path
+        # on its own batch: nothing is shared or skipped between them.
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for r in range(R):
+                step(r, False)
+        singles = []
         for r in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(r, False)
-            graphs.append(g)
+            singles.append(g)
+
+        def replay(n):  # exactly n steps
+            for _ in range(n // R):
+                g_all.replay()
+            for r in range(n % R):
+                singles[r].replay()
+
         # The GPU idles while the graphs are recorded and its clock drops: the
         # first ~100 replays after capture run about 15 % slower. The replays
         # get the same time-based warm-up as the eager steps, then the
-        # requested warm-up replays, before exactly `steps` timed replays.
+        # requested warm-up steps, before exactly `steps` timed steps.
         t0 = time.perf_counter()
-        n_graph_warm = 0
         while time.perf_counter() - t0 < warmup_s:
-            for _ in range(25):
-                graphs[n_graph_warm % R].replay()
-                n_graph_warm += 1
+            replay(25 * R)
+            n_graph_warm += 25 * R
             torch.cuda.synchronize()
-        for i in range(max(warmup, R)):
-            graphs[i % R].replay()
+        replay(max(warmup, R))
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            graphs[i % R].replay()
+        replay(steps)
         torch.cuda.synchronize()
         us_step_graph = (time.perf_counter() - t0) / steps * 1e6
         assert mla.take_device_error() == 0
-        del graphs
+        del g_all, singles
     out = dict(sets=sets, R=R, slots=slots, us_step_eager=us_step_eager, us_step_graph=us_step_graph,
                n_ev=n_ev, t_warm=t_warm, n_time_warm=n_time_warm, n_graph_warm=n_graph_warm,
                median={k: float(np.median(v)) for k, v in per_call.items()},
