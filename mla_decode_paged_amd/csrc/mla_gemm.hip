@@ -34,30 +34,32 @@ constexpr int kBufferWord3G = 0x00020000;  // raw buffer resource: dword data, b
 constexpr int kStoreNT = 2;                 // buffer store cache policy: non-temporal
 
 // LDS bytes of one tile (the staged W tile, then one output plane at a time).
-template <int K, int N, int NT>
+template <int K, int N, int NT, int WAVES = 4>
 constexpr int gemm_smem_bytes() {
   constexpr int kWBytes = K * (NT * 2 + 16);
-  constexpr int kOBytes = kGemmRows * (NT * 2 + 16);
+  constexpr int kOBytes = WAVES * 32 * (NT * 2 + 16);
   return kWBytes > kOBytes ? kWBytes : kOBytes;
 }
 
-// One output tile of the per-head GEMM, by the workgroup with id `bid`.
-template <int K, int N, int NT>
+// One output tile of the per-head GEMM (WAVES x 32 rows), by the workgroup with id `bid`.
+template <int K, int N, int NT, int WAVES = 4>
 __device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo, int R,
                                                int h, int bid, MLA_LDS char* lds) {
   constexpr int kWPitch = NT * 2 + 16;          // bytes per staged W row (k)
   constexpr int kOPitch = NT * 2 + 16;          // bytes per staged output row
-  constexpr int kOBytes = kGemmRows * kOPitch;  // one output plane (hi or lo)
+  constexpr int kRowsWG = WAVES * 32;          // rows of this workgroup's tile
+  constexpr int kThreads = WAVES * 64;
+  constexpr int kOBytes = kRowsWG * kOPitch;    // one output plane (hi or lo)
   constexpr int kNT = NT / 32;                  // 32-column MFMA tiles per wave
   constexpr int kKS = K / 16;                   // k-steps
   // workgroup -> (head, row block, column tile): head = 8 j + (id % 8) for
   // the j-th run of tiles on XCD id % 8
   constexpr int kTilesN = N / NT;
-  const int per_head = kTilesN * ((R + kGemmRows - 1) / kGemmRows);
+  const int per_head = kTilesN * ((R + kRowsWG - 1) / kRowsWG);
   const int idx = bid >> 3, head = (idx / per_head) * 8 + (bid & 7), inner = idx % per_head;
   if (head >= h) return;
-  const int n0 = (inner % kTilesN) * NT, r0 = (inner / kTilesN) * kGemmRows;
+  const int n0 = (inner % kTilesN) * NT, r0 = (inner / kTilesN) * kRowsWG;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, g = lane >> 5, j16 = lane & 15;
 
@@ -65,13 +67,14 @@ __device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, c
   // out first and this lane's row of A behind them, so the W tile can be
   // written to LDS (and the first k-steps multiplied) while A still arrives.
   constexpr int kRowChunks = NT / 8;
-  constexpr int kPer = K * kRowChunks / 256;
+  constexpr int kPer = K * kRowChunks / kThreads;
+  static_assert(K * kRowChunks % kThreads == 0, "W tile split over the threads");
   u32x4 t[kPer];
   {
     const char* wsrc = reinterpret_cast<const char*>(W + (size_t)head * K * N + n0);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int c = threadIdx.x + 256 * i, k = c / kRowChunks, ch = c % kRowChunks;
+      const int c = threadIdx.x + kThreads * i, k = c / kRowChunks, ch = c % kRowChunks;
       t[i] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)k * N * 2 + ch * 16);
     }
   }
@@ -84,7 +87,7 @@ __device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, c
   {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int c = threadIdx.x + 256 * i, k = c / kRowChunks, ch = c % kRowChunks;
+      const int c = threadIdx.x + kThreads * i, k = c / kRowChunks, ch = c % kRowChunks;
       *(MLA_LDS u32x4*)(lds + k * kWPitch + ch * 16) = t[i];
     }
   }
@@ -118,7 +121,7 @@ __device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, c
   constexpr int kRowsPerInstr = 64 / kLanesPerRow;
   const int rr = lane / kLanesPerRow, ch = lane % kLanesPerRow;
   const size_t row_stride = (size_t)h * N * 2;  // bytes between consecutive rows of one head
-  const int valid = min(kGemmRows, R - r0);
+  const int valid = min(kRowsWG, R - r0);
   const unsigned nbytes = (unsigned)((size_t)(valid - 1) * row_stride + NT * 2);
   // the values go to LDS as they are rounded; their residues wait in
   // registers (32 per lane) until the values have left
@@ -157,12 +160,12 @@ __device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, c
   }
 }
 
-template <int K, int N, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(K == kDNope ? 3 : 1))) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+template <int K, int N, int NT, int WAVES = 4>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(K == kDNope ? 3 : 1))) void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                         uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo,
                                                         int R, int h) {
-  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<K, N, NT>()];
-  head_gemm_tile<K, N, NT>(A, W, out, out_lo, R, h, blockIdx.x, (MLA_LDS char*)(smem));
+  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<K, N, NT, WAVES>()];
+  head_gemm_tile<K, N, NT, WAVES>(A, W, out, out_lo, R, h, blockIdx.x, (MLA_LDS char*)(smem));
 }
 
 // The split-KV plan and the query absorption in one launch: the plan reads
@@ -284,14 +287,17 @@ extern "C" int mla_up_v(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o
   if (int rc = check_ptr16(fn, o, "o")) return rc;
   if (int rc = check_shape(fn, b, s_q, h)) return rc;
   const int R = b * s_q;
-  // as in mla_absorb_q: narrower tiles with few heads (h = 32: 7.3 -> 6.9 us), not with 128 (11.6 against 16.7 us)
+  // as in mla_absorb_q: narrower tiles with few heads (h = 32: 7.3 -> 6.9 us), not with 128 (11.6 against 16.7 us);
+  // with few heads also tiles of 64 rows (two waves), which doubles the workgroups to fill every CU
+  // (h = 32, b = 128: 14.1 -> 13.4 us per event-timed call, same outputs)
   const int rb = (R + kGemmRows - 1) / kGemmRows;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int hg = (h + 7) / 8 * 8;
-  if (h <= 32)
-    hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 32>), dim3(kDNope / 32 * rb * hg), dim3(256), 0, st, o_lat,
+  if (h <= 32) {
+    const int rb2 = (R + 63) / 64;
+    hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 32, 2>), dim3(kDNope / 32 * rb2 * hg), dim3(128), 0, st, o_lat,
                        w_uv, o, static_cast<uint16_t*>(nullptr), R, h);
-  else
+  } else
     hipLaunchKernelGGL((head_gemm_kernel<kDLat, kDNope, 64>), dim3(kDNope / 64 * rb * hg), dim3(256), 0, st, o_lat,
                        w_uv, o, static_cast<uint16_t*>(nullptr), R, h);
   if (hipError_t e = hipGetLastError(); e != hipSuccess)
