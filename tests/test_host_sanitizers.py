@@ -54,6 +54,9 @@ def _build():
     for src, p in procs:
         out, _ = p.communicate()
         assert p.returncode == 0, f"compiling {src} with sanitizers failed:\n{out[-4000:]}"
+    for old in os.listdir(OUT_DIR):  # builds of earlier sources
+        if old.startswith("abi_calls_") and not old.endswith(".o"):
+            os.remove(os.path.join(OUT_DIR, old))
     tmp = exe + ".tmp"
     r = subprocess.run([cc, f"--offload-arch={mla_build.ARCH}", *SAN, *objs, "-o", tmp, "-lpthread"],
                        capture_output=True, text=True)
