@@ -41,87 +41,89 @@ constexpr int gemm_smem_bytes() {
   return kWBytes > kOBytes ? kWBytes : kOBytes;
 }
 
-// One output tile of the per-head GEMM (WAVES x 32 rows), by the workgroup with id `bid`.
-template <int K, int N, int NT, int WAVES = 4>
-__device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                               uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo, int R,
-                                               int h, int bid, MLA_LDS char* lds) {
-  constexpr int kWPitch = NT * 2 + 16;          // bytes per staged W row (k)
-  constexpr int kOPitch = NT * 2 + 16;          // bytes per staged output row
-  constexpr int kRowsWG = WAVES * 32;          // rows of this workgroup's tile
-  constexpr int kThreads = WAVES * 64;
-  constexpr int kOBytes = kRowsWG * kOPitch;    // one output plane (hi or lo)
-  constexpr int kNT = NT / 32;                  // 32-column MFMA tiles per wave
-  constexpr int kKS = K / 16;                   // k-steps
-  // workgroup -> (head, row block, column tile): head = 8 j + (id % 8) for
-  // the j-th run of tiles on XCD id % 8
-  constexpr int kTilesN = N / NT;
-  const int per_head = kTilesN * ((R + kRowsWG - 1) / kRowsWG);
-  const int idx = bid >> 3, head = (idx / per_head) * 8 + (bid & 7), inner = idx % per_head;
-  if (head >= h) return;
-  const int n0 = (inner % kTilesN) * NT, r0 = (inner / kTilesN) * kRowsWG;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r32 = lane & 31, g = lane >> 5, j16 = lane & 15;
+// Workgroup -> (head, first row, first column) of its output tile: the tiles
+// of head 8 j + x (its column tiles and row blocks) are consecutive
+// workgroups on XCD x, so they share the A rows and the weight columns
+// through that XCD's L2.
+template <int N, int NT, int WAVES>
+struct TileCoord {
+  int head, r0, n0;
+  __device__ __forceinline__ TileCoord(int bid, int R) {
+    constexpr int kTilesN = N / NT;
+    const int per_head = kTilesN * ((R + WAVES * 32 - 1) / (WAVES * 32));
+    const int idx = bid >> 3, inner = idx % per_head;
+    head = (idx / per_head) * 8 + (bid & 7);
+    n0 = (inner % kTilesN) * NT;
+    r0 = (inner / kTilesN) * (WAVES * 32);
+  }
+};
 
-  // stage W[head][:, n0 : n0 + NT]: K rows of NT * 2 bytes. The W loads go
-  // out first and this lane's row of A behind them, so the W tile can be
-  // written to LDS (and the first k-steps multiplied) while A still arrives.
-  constexpr int kRowChunks = NT / 8;
-  constexpr int kPer = K * kRowChunks / kThreads;
-  static_assert(K * kRowChunks % kThreads == 0, "W tile split over the threads");
+// The weight tile W[head][0:K][n0:n0+NT] (K rows of NT * 2 bytes): load()
+// issues its loads into registers, stage() writes them to LDS (kWPitch bytes
+// per k row), where the MFMA loop reads them back transposed as the A operand.
+template <int K, int N, int NT, int WAVES>
+struct WTile {
+  static constexpr int kPitch = NT * 2 + 16;
+  static constexpr int kRowChunks = NT / 8;
+  static constexpr int kPer = K * kRowChunks / (WAVES * 64);
+  static_assert(K * kRowChunks % (WAVES * 64) == 0, "W tile split over the threads");
   u32x4 t[kPer];
-  {
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ W, int head, int n0) {
     const char* wsrc = reinterpret_cast<const char*>(W + (size_t)head * K * N + n0);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int c = threadIdx.x + kThreads * i, k = c / kRowChunks, ch = c % kRowChunks;
+      const int c = threadIdx.x + WAVES * 64 * i, k = c / kRowChunks, ch = c % kRowChunks;
       t[i] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)k * N * 2 + ch * 16);
     }
   }
-  // this lane's row of A (padding rows repeat the last row and are never stored)
-  const int row = min(r0 + wave * 32 + r32, R - 1);
-  const u32x4* arow = reinterpret_cast<const u32x4*>(A + ((size_t)row * h + head) * K) + g;
-  bf16x8 af[kKS];
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) af[ks] = as_bf16x8(arow[2 * ks]);
-  {
+  __device__ __forceinline__ void stage(MLA_LDS char* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int c = threadIdx.x + kThreads * i, k = c / kRowChunks, ch = c % kRowChunks;
-      *(MLA_LDS u32x4*)(lds + k * kWPitch + ch * 16) = t[i];
+      const int c = threadIdx.x + WAVES * 64 * i, k = c / kRowChunks, ch = c % kRowChunks;
+      *(MLA_LDS u32x4*)(lds + k * kPitch + ch * 16) = t[i];
     }
   }
-  __syncthreads();
-
-  // transposed-read address: k row 16 ks + 8 g + j16/4, column 16*((lane/16)&1) + 4*(j16&3)
-  const int w_off = (8 * g + (j16 >> 2)) * kWPitch + (16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
-  f32x16 c[kNT];
+  // byte offset of this lane's transposed read: k row 16 ks + 8 g + j16/4,
+  // column 16*((lane/16)&1) + 4*(j16&3)
+  static __device__ __forceinline__ int read_offset(int lane) {
+    const int g = lane >> 5, j16 = lane & 15;
+    return (8 * g + (j16 >> 2)) * kPitch + (16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
+  }
+  // k-step ks of the transposed product C^T += W^T A^T: `a` holds 8
+  // consecutive k (16 ks + 8 g ..) of this lane's row of A
+  static __device__ __forceinline__ void kstep(const MLA_LDS char* lds, int w_off, int ks, bf16x8 a,
+                                               f32x16 (&c)[NT / 32]) {
+    const int o = w_off + 16 * ks * kPitch;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) c[t] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    const int o = w_off + 16 * ks * kWPitch;
-#pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-      const bf16x8 wf = cat4(lds_read_tr4(lds, o + 64 * t), lds_read_tr4(lds, o + 64 * t + 4 * kWPitch));
-      c[t] = mfma32(wf, af[ks], c[t]);  // C^T tile t: rows = 32 output columns, columns = 32 rows of A
+    for (int t = 0; t < NT / 32; ++t) {
+      const bf16x8 wf = cat4(lds_read_tr4(lds, o + 64 * t), lds_read_tr4(lds, o + 64 * t + 4 * kPitch));
+      c[t] = mfma32(wf, a, c[t]);  // C^T tile t: rows = 32 output columns, columns = 32 rows of A
     }
   }
-  __syncthreads();  // every wave is done reading the W tile
+};
 
-  // lane holds C^T[column 32 t + 8 q + 4 g + e][row r32], e = 0..3, in c[t][4 q + e]
-  // Each wave stages its own 32 rows in LDS and stores them as row segments
-  // (only its own LDS rows are read back), first the bf16 values, then in
-  // the same rows their rounding residues: a wave's LDS operations complete
-  // in order, so the residue writes follow the reads of the values, and one
-  // plane of LDS suffices. The stores are non-temporal (cache policy nt):
-  // the outputs stream out, and nothing in this kernel reads them back.
+// Epilogue of a tile: lane holds C^T[column 32 t + 8 q + 4 g + e][row r32],
+// e = 0..3, in c[t][4 q + e]. Each wave stages its own 32 rows in LDS and
+// stores them as row segments (only its own LDS rows are read back), first
+// the bf16 values, then (with out_lo) in the same rows their rounding
+// residues: a wave's LDS operations complete in order, so the residue writes
+// follow the reads of the values, and one plane of LDS suffices. The stores
+// are non-temporal (cache policy nt): the outputs stream out, and nothing in
+// these kernels reads them back. Rows past R are dropped by the buffer bounds.
+template <int N, int NT, int WAVES>
+__device__ __forceinline__ void store_tile(const f32x16 (&c)[NT / 32], MLA_LDS char* lds,
+                                           uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo, int R,
+                                           int h, int head, int r0, int n0) {
+  constexpr int kOPitch = NT * 2 + 16;  // bytes per staged output row
+  constexpr int kNT = NT / 32;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31, g = lane >> 5;
   const int orow = wave * 32 + r32;
   constexpr int kLanesPerRow = NT * 2 / 16;
   constexpr int kRowsPerInstr = 64 / kLanesPerRow;
   const int rr = lane / kLanesPerRow, ch = lane % kLanesPerRow;
   const size_t row_stride = (size_t)h * N * 2;  // bytes between consecutive rows of one head
-  const int valid = min(kRowsWG, R - r0);
+  const int valid = min(WAVES * 32, R - r0);
   const unsigned nbytes = (unsigned)((size_t)(valid - 1) * row_stride + NT * 2);
   // the values go to LDS as they are rounded; their residues wait in
   // registers (32 per lane) until the values have left
@@ -158,6 +160,41 @@ __device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, c
         *reinterpret_cast<MLA_LDS bf16x4*>(lds + orow * kOPitch + (32 * t + 8 * q + 4 * g) * 2) = vlo[4 * t + q];
     store_rows(out_lo);
   }
+}
+
+// One output tile of the per-head GEMM (WAVES x 32 rows), by the workgroup with id `bid`.
+template <int K, int N, int NT, int WAVES = 4>
+__device__ __forceinline__ void head_gemm_tile(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                               uint16_t* __restrict__ out, uint16_t* __restrict__ out_lo, int R,
+                                               int h, int bid, MLA_LDS char* lds) {
+  constexpr int kKS = K / 16;  // k-steps
+  const TileCoord<N, NT, WAVES> tc(bid, R);
+  if (tc.head >= h) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31, g = lane >> 5;
+
+  // The W loads go out first and this lane's row of A behind them, so the W
+  // tile can be written to LDS (and the first k-steps multiplied) while A
+  // still arrives.
+  WTile<K, N, NT, WAVES> wt;
+  wt.load(W, tc.head, tc.n0);
+  // this lane's row of A (padding rows repeat the last row and are never stored)
+  const int row = min(tc.r0 + wave * 32 + r32, R - 1);
+  const u32x4* arow = reinterpret_cast<const u32x4*>(A + ((size_t)row * h + tc.head) * K) + g;
+  bf16x8 af[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) af[ks] = as_bf16x8(arow[2 * ks]);
+  wt.stage(lds);
+  __syncthreads();
+
+  const int w_off = WTile<K, N, NT, WAVES>::read_offset(lane);
+  f32x16 c[NT / 32];
+#pragma unroll
+  for (int t = 0; t < NT / 32; ++t) c[t] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) WTile<K, N, NT, WAVES>::kstep(lds, w_off, ks, af[ks], c);
+  __syncthreads();  // every wave is done reading the W tile
+  store_tile<N, NT, WAVES>(c, lds, out, out_lo, R, h, tc.head, tc.r0, tc.n0);
 }
 
 template <int K, int N, int NT, int WAVES = 4>
