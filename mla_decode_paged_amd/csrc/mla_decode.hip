@@ -1044,23 +1044,28 @@ void mla_decode_tsplit_kernel(DecodeParams P) {
 // (every lane has 16 loads in flight across its rows); R = 1 gives a
 // sequence cut into many pieces 4x more waves, so each row's chain of
 // dependent groups is 4x shorter.
+// As in the decode kernels every branch is uniform over the wave: the piece
+// count is a scalar load, a row without visible keys is weighed by arithmetic
+// rather than skipped, and the lanes of a row all store its lse.
 template <int R>
 __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
   constexpr int kLanesPerRow = 64 / R;
   constexpr int kGroup = 16 / R;  // pieces of every row whose loads are in flight together
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.y * (4 * R) + wave_id_uniform() * R + lane / kLanesPerRow;
+  const int wrow0 = blockIdx.y * (4 * R) + wave_id_uniform() * R;  // first row of this wave
+  // M is a multiple of 16, so a wave's R rows all lie inside it or all past it
+  if (wrow0 >= P.M) return;
+  const int row = wrow0 + lane / kLanesPerRow;
   const int t = lane % kLanesPerRow;
-  if (row >= P.M) return;
-  const int ns0 = P.num_splits[b], n = P.num_splits[b + 1] - ns0;
+  const int ns0 = ldc(P.num_splits + b), n = ldc(P.num_splits + b + 1) - ns0;
   if (n == 1) return;
   const long long orow = (long long)b * P.M + row;
   u32x4* out = reinterpret_cast<u32x4*>(P.o_lat + orow * kDLat) + t;
   if (n == 0) {
 #pragma unroll
     for (int q = 0; q < R; ++q) out[kLanesPerRow * q] = u32x4{};
-    if (t == 0) P.lse[orow] = -INFINITY;
+    P.lse[orow] = -INFINITY;
     return;
   }
   // The lo residue of the row (first-order lse correction, see the decode
@@ -1068,8 +1073,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
   // passes under the merge; with four, after it (its registers would cost a
   // wave per SIMD during the merge).
   u32x4 q8[R];
-  const u32x4* qlo = P.q_lat_lo != nullptr ? reinterpret_cast<const u32x4*>(P.q_lat_lo + orow * kDLat) + t : nullptr;
-  if (R == 1 && qlo != nullptr) {
+  const bool has_lo = P.q_lat_lo != nullptr;  // uniform (a test of a per-lane pointer would not be)
+  const u32x4* qlo = reinterpret_cast<const u32x4*>(P.q_lat_lo + orow * kDLat) + t;
+  if (R == 1 && has_lo) {
 #pragma unroll
     for (int q = 0; q < R; ++q) q8[q] = qlo[kLanesPerRow * q];
   }
@@ -1101,14 +1107,16 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
     float m_new = mx;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) m_new = fmaxf(m_new, lk[i]);
-    if (m_new == -INFINITY) continue;  // nothing visible yet (uniform over the row's lanes)
-    const float alpha = fast_exp2((mx - m_new) * 1.4426950408889634f);  // 0 when mx = -inf
+    // While a row has seen nothing (m_new = -inf) every weight below is 0
+    // and its sums stay 0, as if the group were skipped.
+    const float m_s = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2((mx - m_s) * 1.4426950408889634f);  // 0 when mx = -inf
     wsum *= alpha;
 #pragma unroll
     for (int v = 0; v < 8 * R; ++v) o[v] *= alpha;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
-      const float w = fast_exp2((lk[i] - m_new) * 1.4426950408889634f);  // 0 for the empty tail
+      const float w = fast_exp2((lk[i] - m_s) * 1.4426950408889634f);  // 0 for the empty tail
       wsum += w;
       const float ws = w * sk[i];
 #pragma unroll
@@ -1124,7 +1132,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float dot = 0.f;  // q_lo . o_lat
-  if (R != 1 && qlo != nullptr) {
+  if (R != 1 && has_lo) {
 #pragma unroll
     for (int q = 0; q < R; ++q) q8[q] = qlo[kLanesPerRow * q];
   }
@@ -1134,7 +1142,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = (__bf16)(o[8 * q + e] * inv);
     out[kLanesPerRow * q] = __builtin_bit_cast(u32x4, w);
-    if (qlo != nullptr) {
+    if (has_lo) {
       const bf16x8 qv = __builtin_bit_cast(bf16x8, q8[q]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot += o[8 * q + e] * inv * (float)qv[e];
@@ -1142,8 +1150,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(DecodeParams P) {
   }
 #pragma unroll
   for (int m = kLanesPerRow / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);  // the row's lanes
-  if (t == 0)
-    P.lse[orow] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 + P.scale * dot : -INFINITY;
+  P.lse[orow] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 + P.scale * dot : -INFINITY;  // same value from each lane
 }
 
 // The page loader on its own: one workgroup per (page, sequence).
